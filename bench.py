@@ -1,0 +1,188 @@
+"""Benchmark of the all-reduce hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grad7b]
+                    [--mode fused|stepwise] [--no-cpu-baseline]
+
+One "step" is one in-place all-reduce of the whole workload: every virtual
+rank's buffer (inputs already resident in HBM) reduced and the result
+written back to every rank. The default workload is the 7e9-element fp16
+gradient per rank (14 GB, the 7B model of the geek-doc page "训练梯度同步与
+集合通信", sections 一 and 四) at 8 virtual ranks, AVG with fp32
+accumulation, fused mode.
+
+Reported (one JSON line):
+  value        algbw = S / T, S = bytes per rank (handbook "集合通信原语",
+               section 算法带宽与总线带宽)
+  busbw        algbw * 2(N-1)/N (same section)
+  roofline     the fused kernel's algorithmic HBM bytes 2*N*S per launch
+               (each rank's input read once, N outputs written once) over its
+               average launch time, against the 8 TB/s HBM peak; traffic =
+               bytes the HBM counters saw per launch (rocprofv3 FETCH_SIZE +
+               WRITE_SIZE, scaled by a plain copy's reading), from the
+               committed profile when it matches the current kernel source,
+               else null
+  cpu_baseline the CPU oracle (the literal ring, one thread) on a window of
+               the same workload, in the same unit
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "all-reduce algbw/busbw GB/s and % HBM peak, N=8 ranks, 64 MiB–14 GB msgs"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "ring_all_reduce_ar_amd", "csrc", "kernels.hip")
+
+# workload name -> (nranks, count, dtype, op, description)
+WORKLOADS = {
+    "grad7b": (8, 7_000_000_000, "f16", "avg",
+               "grad7b: 8 virtual ranks x 7e9 fp16 gradient (14 GB per rank), N(0,1e-3^2) with 1% N(0,1) "
+               "outliers, AVG with fp32 accumulation, in place"),
+    "bucket25": (8, 6_553_600, "f32", "avg",
+                 "bucket25: 8 virtual ranks x one 25 MiB fp32 DDP bucket, N(0,1e-3^2), AVG, in place"),
+    "sweep64m": (8, 16_777_216, "f32", "sum", "sweep point: 8 virtual ranks x 64 MiB fp32, uniform[-1,1), SUM, in place"),
+    "sweep256m": (8, 67_108_864, "f32", "sum",
+                  "sweep point: 8 virtual ranks x 256 MiB fp32, uniform[-1,1), SUM, in place"),
+    "bucket64": (64, 67_108_864, "f32", "max",
+                 "bucket64: 64 virtual ranks x 256 MiB fp32 bucket, uniform[-1,1), MAX, in place"),
+}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4}
+CPU_WINDOW_LOG2 = 26  # elements per rank in the CPU oracle's window
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, mode: str):
+    """Per-launch HBM bytes from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m = re.search(r"kernel_sha:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_sha():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(nranks: int, dtype: str, op: str, workload: str):
+    """The oracle's literal ring on the first 2^26 elements per rank of the
+    same workload (seeded the same way), timed on one host thread."""
+    import oracle
+    import synthetic
+    count = 1 << CPU_WINDOW_LOG2
+    wl = workload if workload in synthetic.WORKLOAD_IDS else "sweep"
+    xs = [synthetic.to_numpy(t) for t in synthetic.rank_inputs(wl, nranks, count, dtype, op=op)]
+    t0 = time.perf_counter()
+    oracle.ring_all_reduce(xs, dtype, op)
+    dt = time.perf_counter() - t0
+    s_bytes = count * ESIZE[dtype]
+    return {"value": s_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nranks} ranks x 2^{CPU_WINDOW_LOG2} {dtype} elements per rank ({s_bytes / 2**20:.0f} MiB), "
+                      f"literal ring (N-1 reduce-scatter + N-1 all-gather steps), {op}, single thread",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="grad7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: the N virtual ranks of this all-reduce live on one "
+              f"GPU as separate HBM buffers, and no figure across several GPUs is produced. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ring_all_reduce_ar_amd as ar
+    import synthetic
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    n, count, dtype, op, desc = WORKLOADS[args.workload]
+    wl = args.workload if args.workload in synthetic.WORKLOAD_IDS else "sweep"
+    print(f"[bench] generating {desc}", file=sys.stderr, flush=True)
+    bufs = synthetic.rank_inputs(wl, n, count, dtype, device="cuda", op=op)
+    comm = ar.Comm(n, 0)
+    ws = None
+    need = ar.ar_workspace_bytes(ar.AR_COLL_ALL_REDUCE, n, count, dtype, args.mode)
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        ar.ar_comm_set_workspace(comm, ws)
+    ptrs = [b.data_ptr() for b in bufs]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ar.ar_all_reduce(comm, ptrs, ptrs, count, dtype, op, args.mode, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    s_bytes = count * ESIZE[dtype]
+    algbw = s_bytes / (ms * 1e-3) / 1e9
+    busbw = algbw * 2 * (n - 1) / n
+    # fused: one launch per step; stepwise: 2(N-1) launches, reported against
+    # the same algorithmic bytes so the two modes compare directly.
+    alg_bytes = 2 * n * s_bytes
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, args.mode)
+    result = {
+        "metric": METRIC,
+        "value": round(algbw, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": desc, "nranks": n, "count_per_rank": count, "bytes_per_rank": s_bytes, "op": op,
+                   "mode": args.mode, "accumulate": "f32" if dtype in ("f16", "bf16") else dtype,
+                   "parallelism": f"{n} virtual ranks on 1 GPU"},
+        "busbw": round(busbw, 3),
+        "hbm_gbps": round(achieved, 1),
+        "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+    del bufs, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

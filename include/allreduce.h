@@ -1,0 +1,172 @@
+/*
+ * allreduce.h -- C ABI of liballreduce, a ring all-reduce engine for one
+ * AMD Instinct MI355X (gfx950) on which N "virtual ranks" are N separate
+ * device buffers.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] mhpq.cn news/451051, article on how all-reduce keeps every card's
+ *       model identical: s2.1 (all-reduce semantics; SUM, AVG = sum then
+ *       divide by N, MAX, MIN, PROD), s2.2 (every rank takes part with
+ *       matching shapes; deterministic result), s3.2 (ring = reduce-scatter
+ *       then all-gather), s5.3 (reduce fp16/bf16 gradients in fp32).
+ *  [P2] xxqk.cn news/376101, article on AllReduce bottlenecks: s4.3 (do not
+ *       mix dtypes inside one reduction).
+ *  [P3] geek-doc.cn, "训练梯度同步与集合通信:从参数服务器到 Ring AllReduce":
+ *       section 三 (the two ring phases of N-1 steps each), section 四
+ *       (2(N-1)/N * M bytes per rank; alpha-beta model), section 六
+ *       (reduce-scatter and all-gather used on their own, as in ZeRO/FSDP).
+ *  [P4] anrans.github.io handbook, "集合通信原语": section 五个原语
+ *       (all_reduce, reduce_scatter_tensor gives rank r block r,
+ *       all_gather_into_tensor concatenates in rank order), section
+ *       环形 all-reduce 与通信量 (the ring's index schedule), section α-β 模型
+ *       (one-shot direct-read all-reduce for small messages).
+ *
+ * The pages' interface is one call per process and rank. Here one call
+ * carries every rank's buffer: sendbufs[r] / recvbufs[r] are rank r's
+ * device buffers, r = 0..nranks-1, so no rank can miss the call.
+ *
+ * Conventions for every entry point:
+ *  - Pointers in sendbufs[] / recvbufs[] are device pointers on the comm's
+ *    device; the arrays themselves are host memory, read only during the
+ *    call. The caller owns all device memory, the workspace and the stream,
+ *    and keeps them alive until the enqueued work has completed.
+ *  - Calls are stream-ordered and asynchronous: they return once the work is
+ *    enqueued on `stream` (NULL = the device's null stream).
+ *  - Errors are returned, never raised: no call aborts or exits. A failing
+ *    call enqueues nothing, except AR_ERR_HIP, which reports a launch error
+ *    after earlier steps may have been enqueued. ar_last_error() gives a
+ *    thread-local message for the last failure.
+ *  - count == 0 (or recvcount/sendcount == 0) is a successful no-op.
+ *  - Results are deterministic: the same inputs give the same bits on every
+ *    call and in both modes.
+ */
+#ifndef LIBALLREDUCE_ALLREDUCE_H
+#define LIBALLREDUCE_ALLREDUCE_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_MAX_RANKS 64
+
+typedef struct ar_comm* ar_comm_t;
+
+typedef enum {
+    AR_SUCCESS = 0,
+    AR_ERR_INVALID_ARGUMENT = 1, /* bad pointer, enum, size, alias or workspace */
+    AR_ERR_UNSUPPORTED = 2,      /* a valid request this build does not serve */
+    AR_ERR_HIP = 3,              /* a HIP runtime call or kernel launch failed */
+    AR_ERR_OUT_OF_MEMORY = 4,    /* host allocation for the comm failed */
+    AR_ERR_INTERNAL = 5
+} ar_result_t;
+
+/* Storage types. fp16 and bf16 are reduced in fp32 and rounded once, to
+ * nearest even, at the end [P1 s5.3]; int32 wraps modulo 2^32. One dtype
+ * per call [P2 s4.3]. */
+typedef enum { AR_FLOAT32 = 0, AR_FLOAT16 = 1, AR_BFLOAT16 = 2, AR_INT32 = 3 } ar_dtype_t;
+
+/* Reduce ops [P1 s2.1]. AVG is the sum divided once by nranks (fp: one
+ * correctly rounded fp32 divide; int32: truncation toward zero). MAX/MIN
+ * return NaN when either operand is NaN and order +0 above -0. */
+typedef enum { AR_SUM = 0, AR_AVG = 1, AR_MAX = 2, AR_MIN = 3, AR_PROD = 4 } ar_op_t;
+
+/* AR_MODE_FUSED: one launch that reads every rank's element once and writes
+ * the result to every output -- the direct-read ("one-shot") pattern [P4
+ * section α-β 模型] -- folding the ranks in ring order, so its bits equal the
+ * ring's.
+ * AR_MODE_RING_STEPWISE: the ring itself, one launch per ring step:
+ * N-1 reduce-scatter steps then N-1 all-gather steps [P3 section 三;
+ * P4 section 环形 all-reduce 与通信量]. */
+typedef enum { AR_MODE_FUSED = 0, AR_MODE_RING_STEPWISE = 1 } ar_mode_t;
+
+typedef enum { AR_COLL_ALL_REDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GATHER = 2 } ar_collective_t;
+
+/* Create a communicator for `nranks` (1..AR_MAX_RANKS) virtual ranks on HIP
+ * device `hip_device`. On success *comm owns host state and a few HIP
+ * events; release it with ar_comm_destroy. Errors: INVALID_ARGUMENT for a
+ * NULL comm pointer or nranks out of range, HIP if the device cannot be
+ * queried, OUT_OF_MEMORY. */
+ar_result_t ar_comm_create(ar_comm_t* comm, int nranks, int hip_device);
+
+/* Destroy a communicator (NULL is a no-op). Work already enqueued that uses
+ * it must have completed. */
+ar_result_t ar_comm_destroy(ar_comm_t comm);
+
+/* Number of ranks the communicator was created with, or -1 for NULL. */
+int ar_comm_nranks(ar_comm_t comm);
+
+/* Device workspace (bytes) a call needs; 0 when none. `count` is the
+ * collective's own count argument (count, recvcount or sendcount).
+ * Stepwise all-reduce of fp16/bf16 keeps fp32 partial sums: 4*count bytes.
+ * Stepwise reduce-scatter keeps the partials of all nranks blocks:
+ * 4*nranks*recvcount bytes. Everything else: 0. Returns (size_t)-1 for
+ * invalid arguments or if the size overflows. */
+size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype, ar_mode_t mode);
+
+/* Attach a caller-owned device workspace (16-byte aligned, `bytes` long) to
+ * the communicator; NULL/0 detaches it. The library never allocates device
+ * memory itself. Calls that share a workspace must be ordered on one
+ * stream. Errors: INVALID_ARGUMENT for a NULL comm, a misaligned pointer,
+ * or bytes > 0 with a NULL pointer. */
+ar_result_t ar_comm_set_workspace(ar_comm_t comm, void* dev_ptr, size_t bytes);
+
+/* All-reduce [P1 s2.1; P3 section 三; P4 section 五个原语]: after the call
+ * recvbufs[r][i] = op over ranks of sendbufs[r][i], i < count, identical for
+ * every r. Chunk c of the ring is elements [c*q, min((c+1)*q, count)) with
+ * q = ceil(count/nranks), and chunk c is folded in rank order
+ * c, c+1, ..., c+nranks-1 (mod nranks): acc = x_c; acc = x_{c+k} (+) acc.
+ * sendbufs[r] and recvbufs[r] each hold `count` elements of `dtype`.
+ * In place is allowed (sendbufs[r] == recvbufs[r]); any other overlap
+ * between any two of the 2*nranks buffers (or the workspace) is
+ * INVALID_ARGUMENT. Stepwise fp16/bf16 needs a workspace of
+ * ar_workspace_bytes(...) bytes, else INVALID_ARGUMENT. Pointers need not
+ * be aligned; 16-byte alignment with q a multiple of 16/sizeof(dtype)
+ * selects the vector kernels. */
+ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
+                          ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
+
+/* Reduce-scatter [P3 section 六; P4 section 五个原语]: sendbufs[r] holds
+ * nranks*recvcount elements; recvbufs[c] (recvcount elements) receives
+ * block c of the reduction, block c being folded in the same ring order as
+ * in ar_all_reduce, so reduce-scatter followed by all-gather equals
+ * all-reduce bit for bit. In place: recvbufs[r] == sendbufs[r] +
+ * r*recvcount elements. Stepwise mode needs a workspace of
+ * ar_workspace_bytes(...) bytes. Errors as ar_all_reduce. */
+ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
+                              size_t recvcount, ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
+
+/* All-gather [P3 section 六; P4 section 五个原语]: sendbufs[r] holds
+ * sendcount elements; every recvbufs[r] (nranks*sendcount elements)
+ * receives the nranks send blocks in rank order. In place:
+ * sendbufs[r] == recvbufs[r] + r*sendcount elements. Errors as
+ * ar_all_reduce (no workspace is needed). */
+ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t sendcount,
+                          ar_dtype_t dtype, ar_mode_t mode, hipStream_t stream);
+
+/* Per-step timing of stepwise calls (the alpha-beta model's per-step cost,
+ * [P3 section 四; P4 section α-β 模型]). When enabled, each stepwise call
+ * records a HIP event before its first step and after every step; fused
+ * calls record one interval. Recording adds a little per-step overhead and
+ * is not meant for graph capture. */
+ar_result_t ar_comm_set_step_timing(ar_comm_t comm, int enable);
+
+/* Step durations (ms) of the last timed call on this comm: waits for that
+ * call's last event, writes min(cap, steps) values to out and the step
+ * count to *nsteps. INVALID_ARGUMENT if timing was off or nothing was
+ * timed yet. */
+ar_result_t ar_last_step_times_ms(ar_comm_t comm, float* out, int cap, int* nsteps);
+
+/* Static description of a result code. */
+const char* ar_result_string(ar_result_t result);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char* ar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBALLREDUCE_ALLREDUCE_H */

@@ -1,0 +1,580 @@
+// api.cpp -- the C ABI of liballreduce (include/allreduce.h): argument
+// checks, the ring plan (chunk partition and step schedule), mode dispatch,
+// per-step event timing and thread-local error text. Every check runs before
+// the first HIP call, so a rejected call touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "allreduce.h"
+#include "kernels.h"
+
+#define AR_EXPORT extern "C" __attribute__((visibility("default")))
+
+struct ar_comm {
+    int nranks = 0;
+    int device = 0;
+    int num_cus = 256;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    bool debug = false;
+    bool step_timing = false;
+    std::vector<hipEvent_t> events;  // step boundaries of the last timed call
+    int last_steps = -1;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ar_result_t fail(ar_result_t code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+ar_result_t hip_fail(hipError_t e, const char* what)
+{
+    return fail(AR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(ar_dtype_t d)
+{
+    switch (d) {
+    case AR_FLOAT32: return 4;
+    case AR_FLOAT16: return 2;
+    case AR_BFLOAT16: return 2;
+    case AR_INT32: return 4;
+    }
+    return 0;
+}
+
+bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
+bool valid_op(int o) { return o >= AR_SUM && o <= AR_PROD; }
+bool valid_mode(int m) { return m == AR_MODE_FUSED || m == AR_MODE_RING_STEPWISE; }
+
+const char* dtype_name(ar_dtype_t d)
+{
+    static const char* names[] = {"fp32", "fp16", "bf16", "int32"};
+    return valid_dtype(d) ? names[d] : "?";
+}
+
+// a * b without overflow, else false.
+bool mul_ok(size_t a, size_t b, size_t* out)
+{
+    if (a != 0 && b > SIZE_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev)
+    {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+        else if (err == hipSuccess) prev = -1;
+    }
+    ~DeviceGuard()
+    {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+struct Interval {
+    uintptr_t lo, hi;
+    const char* what;
+    int rank;
+};
+
+// The 2n rank buffers (plus the workspace) must not overlap, except that a
+// rank's send buffer may sit at `inplace_off` bytes into its recv buffer
+// (all-reduce: 0; all-gather: r*sendbytes) or its recv buffer at
+// `inplace_off` bytes into its send buffer (reduce-scatter: r*recvbytes).
+ar_result_t check_buffers(int n, const void* const send[], void* const recv[], size_t send_bytes, size_t recv_bytes,
+                          int coll, size_t elem, const void* ws, size_t ws_need)
+{
+    std::vector<Interval> iv;
+    iv.reserve(2 * n + 1);
+    for (int r = 0; r < n; ++r) {
+        if (!send[r]) return fail(AR_ERR_INVALID_ARGUMENT, "sendbufs[%d] is NULL", r);
+        if (!recv[r]) return fail(AR_ERR_INVALID_ARGUMENT, "recvbufs[%d] is NULL", r);
+        if (reinterpret_cast<uintptr_t>(send[r]) % elem || reinterpret_cast<uintptr_t>(recv[r]) % elem)
+            return fail(AR_ERR_INVALID_ARGUMENT, "rank %d buffer is not aligned to the %zu-byte element size", r, elem);
+        const uintptr_t s = reinterpret_cast<uintptr_t>(send[r]);
+        const uintptr_t d = reinterpret_cast<uintptr_t>(recv[r]);
+        if (s > UINTPTR_MAX - send_bytes || d > UINTPTR_MAX - recv_bytes)
+            return fail(AR_ERR_INVALID_ARGUMENT, "rank %d buffer wraps the address space", r);
+        bool inplace = false;
+        if (coll == AR_COLL_ALL_REDUCE) inplace = (s == d);
+        else if (coll == AR_COLL_REDUCE_SCATTER) inplace = (d == s + static_cast<uintptr_t>(r) * recv_bytes);
+        else inplace = (s == d + static_cast<uintptr_t>(r) * send_bytes);
+        if (inplace) {
+            iv.push_back({std::min(s, d), std::max(s + send_bytes, d + recv_bytes), "in-place buffer", r});
+        } else {
+            iv.push_back({s, s + send_bytes, "sendbufs", r});
+            iv.push_back({d, d + recv_bytes, "recvbufs", r});
+        }
+    }
+    if (ws_need) iv.push_back({reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + ws_need, "workspace", -1});
+    std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < iv.size(); ++i) {
+        if (iv[i].lo < iv[i - 1].hi && iv[i].hi > iv[i].lo && iv[i - 1].hi > iv[i - 1].lo)
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s[%d] overlaps %s[%d] (only the documented in-place layout may alias)",
+                        iv[i].what, iv[i].rank, iv[i - 1].what, iv[i - 1].rank);
+    }
+    return AR_SUCCESS;
+}
+
+// Workgroups per chunk row: enough to cover the chunk, capped so that the
+// whole grid is a few waves of workgroups per CU (grid-stride loops take the
+// rest).
+int grid_for(const ar_comm* comm, uint64_t units_per_row, int rows)
+{
+    const uint64_t want = std::max<uint64_t>(1, ceil_div(units_per_row, ar::kBlock));
+    const uint64_t cap = std::max<uint64_t>(1, static_cast<uint64_t>(comm->num_cus) * 8 / std::max(1, rows));
+    return static_cast<int>(std::min(want, cap));
+}
+
+// Records the start of a call and the end of each step when timing is on.
+struct StepTimer {
+    ar_comm* comm;
+    hipStream_t stream;
+    int steps = 0;
+    StepTimer(ar_comm* c, hipStream_t s) : comm(c), stream(s) {}
+    hipError_t ensure(int nsteps)
+    {
+        while (static_cast<int>(comm->events.size()) < nsteps + 1) {
+            hipEvent_t e;
+            hipError_t err = hipEventCreate(&e);
+            if (err != hipSuccess) return err;
+            comm->events.push_back(e);
+        }
+        return hipSuccess;
+    }
+    hipError_t begin(int nsteps)
+    {
+        if (!comm->step_timing) return hipSuccess;
+        comm->last_steps = -1;
+        hipError_t err = ensure(nsteps);
+        if (err != hipSuccess) return err;
+        return hipEventRecord(comm->events[0], stream);
+    }
+    hipError_t step()
+    {
+        if (!comm->step_timing) return hipSuccess;
+        ++steps;
+        return hipEventRecord(comm->events[steps], stream);
+    }
+    void end()
+    {
+        if (comm->step_timing) comm->last_steps = steps;
+    }
+};
+
+ar_result_t check_common(ar_comm_t comm, const void* const* send, void* const* recv, int dtype, int mode)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
+    if (!send) return fail(AR_ERR_INVALID_ARGUMENT, "sendbufs array is NULL");
+    if (!recv) return fail(AR_ERR_INVALID_ARGUMENT, "recvbufs array is NULL");
+    if (!valid_dtype(dtype)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid dtype %d", dtype);
+    if (!valid_mode(mode)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid mode %d", mode);
+    return AR_SUCCESS;
+}
+
+ar_result_t need_workspace(const ar_comm* comm, size_t need)
+{
+    if (need == 0) return AR_SUCCESS;
+    if (!comm->ws || comm->ws_bytes < need)
+        return fail(AR_ERR_INVALID_ARGUMENT,
+                    "this call needs a device workspace of %zu bytes (attached: %zu); see ar_workspace_bytes", need,
+                    comm->ws ? comm->ws_bytes : static_cast<size_t>(0));
+    return AR_SUCCESS;
+}
+
+template <class Args>
+void fill_ptrs(Args& a, int n, const void* const send[], void* const recv[])
+{
+    for (int r = 0; r < n; ++r) {
+        a.send[r] = send[r];
+        a.recv[r] = recv[r];
+    }
+}
+
+bool all_aligned16(int n, const void* const send[], void* const recv[])
+{
+    for (int r = 0; r < n; ++r)
+        if (!aligned16(send[r]) || !aligned16(recv[r])) return false;
+    return true;
+}
+
+// Local copies send[r] -> recv[r] + r*dst_stride for ranks whose buffers differ.
+ar_result_t local_copies(ar_comm* comm, int n, const void* const send[], void* const recv[], size_t bytes,
+                         size_t dst_stride, hipStream_t stream)
+{
+    ar::CopyArgs a{};
+    int m = 0;
+    bool vec = (bytes % 16 == 0) && (dst_stride % 16 == 0);
+    for (int r = 0; r < n; ++r) {
+        const char* dst = static_cast<const char*>(recv[r]) + static_cast<size_t>(r) * dst_stride;
+        if (dst == send[r]) continue;
+        // Pack only the ranks that need a copy; rank index m keeps dst offset r*dst_stride
+        // by pre-offsetting the destination pointer.
+        a.send[m] = send[r];
+        a.recv[m] = const_cast<char*>(dst);
+        vec = vec && aligned16(send[r]) && aligned16(dst);
+        ++m;
+    }
+    if (m == 0) return AR_SUCCESS;
+    a.n = m;
+    a.total = bytes;
+    a.dst_stride = 0;
+    hipError_t e = ar::launch_local_copy(a, vec, grid_for(comm, vec ? ceil_div(bytes, 16) : ceil_div(bytes, 2), m), stream);
+    return e == hipSuccess ? AR_SUCCESS : hip_fail(e, "local copy launch");
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// communicator
+// ---------------------------------------------------------------------------
+AR_EXPORT ar_result_t ar_comm_create(ar_comm_t* comm, int nranks, int hip_device)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm pointer is NULL");
+    *comm = nullptr;
+    if (nranks < 1 || nranks > AR_MAX_RANKS)
+        return fail(AR_ERR_INVALID_ARGUMENT, "nranks %d is outside 1..%d", nranks, AR_MAX_RANKS);
+    if (hip_device < 0) return fail(AR_ERR_INVALID_ARGUMENT, "hip_device %d is negative", hip_device);
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (hip_device >= ndev) return fail(AR_ERR_INVALID_ARGUMENT, "hip_device %d but %d devices", hip_device, ndev);
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, hip_device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    ar_comm* c = new (std::nothrow) ar_comm();
+    if (!c) return fail(AR_ERR_OUT_OF_MEMORY, "cannot allocate the communicator");
+    c->nranks = nranks;
+    c->device = hip_device;
+    c->num_cus = cus > 0 ? cus : 256;
+    const char* dbg = std::getenv("AR_DEBUG");
+    c->debug = dbg && *dbg && std::strcmp(dbg, "0") != 0;
+    *comm = c;
+    return AR_SUCCESS;
+}
+
+AR_EXPORT ar_result_t ar_comm_destroy(ar_comm_t comm)
+{
+    if (!comm) return AR_SUCCESS;
+    for (hipEvent_t e : comm->events) (void)hipEventDestroy(e);
+    delete comm;
+    return AR_SUCCESS;
+}
+
+AR_EXPORT int ar_comm_nranks(ar_comm_t comm) { return comm ? comm->nranks : -1; }
+
+AR_EXPORT size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype, ar_mode_t mode)
+{
+    if (nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype(dtype) || !valid_mode(mode)) return static_cast<size_t>(-1);
+    if (mode != AR_MODE_RING_STEPWISE || nranks == 1) return 0;
+    size_t out = 0;
+    if (coll == AR_COLL_ALL_REDUCE) {
+        if (dtype != AR_FLOAT16 && dtype != AR_BFLOAT16) return 0;
+        return mul_ok(count, 4, &out) ? out : static_cast<size_t>(-1);
+    }
+    if (coll == AR_COLL_REDUCE_SCATTER) {
+        size_t total = 0;
+        if (!mul_ok(count, static_cast<size_t>(nranks), &total) || !mul_ok(total, 4, &out))
+            return static_cast<size_t>(-1);
+        return out;
+    }
+    if (coll == AR_COLL_ALL_GATHER) return 0;
+    return static_cast<size_t>(-1);
+}
+
+AR_EXPORT ar_result_t ar_comm_set_workspace(ar_comm_t comm, void* dev_ptr, size_t bytes)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
+    if (bytes > 0 && !dev_ptr) return fail(AR_ERR_INVALID_ARGUMENT, "workspace of %zu bytes at NULL", bytes);
+    if (dev_ptr && !aligned16(dev_ptr)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+    comm->ws = bytes ? dev_ptr : nullptr;
+    comm->ws_bytes = dev_ptr ? bytes : 0;
+    return AR_SUCCESS;
+}
+
+AR_EXPORT ar_result_t ar_comm_set_step_timing(ar_comm_t comm, int enable)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
+    comm->step_timing = enable != 0;
+    comm->last_steps = -1;
+    return AR_SUCCESS;
+}
+
+AR_EXPORT ar_result_t ar_last_step_times_ms(ar_comm_t comm, float* out, int cap, int* nsteps)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
+    if (!nsteps || (cap > 0 && !out)) return fail(AR_ERR_INVALID_ARGUMENT, "NULL output pointer");
+    if (!comm->step_timing || comm->last_steps < 0)
+        return fail(AR_ERR_INVALID_ARGUMENT, "no timed call on this comm (enable ar_comm_set_step_timing first)");
+    DeviceGuard g(comm->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    const int k = comm->last_steps;
+    *nsteps = k;
+    if (k == 0) return AR_SUCCESS;
+    hipError_t e = hipEventSynchronize(comm->events[k]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (int i = 0; i < k && i < cap; ++i) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, comm->events[i], comm->events[i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        out[i] = ms;
+    }
+    return AR_SUCCESS;
+}
+
+// ---------------------------------------------------------------------------
+// collectives
+// ---------------------------------------------------------------------------
+AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
+                                    ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
+{
+    ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
+    if (rc != AR_SUCCESS) return rc;
+    if (!valid_op(op)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid op %d", static_cast<int>(op));
+    const int n = comm->nranks;
+    const size_t e = elem_size(dtype);
+    size_t bytes = 0;
+    if (!mul_ok(count, e, &bytes)) return fail(AR_ERR_INVALID_ARGUMENT, "count %zu overflows", count);
+    if (count == 0) return AR_SUCCESS;
+    const bool stepwise = mode == AR_MODE_RING_STEPWISE && n > 1;
+    const size_t ws_need = stepwise ? ar_workspace_bytes(AR_COLL_ALL_REDUCE, n, count, dtype, mode) : 0;
+    if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    rc = need_workspace(comm, ws_need);
+    if (rc != AR_SUCCESS) return rc;
+    rc = check_buffers(n, sendbufs, recvbufs, bytes, bytes, AR_COLL_ALL_REDUCE, e, comm->ws, ws_need);
+    if (rc != AR_SUCCESS) return rc;
+
+    // Ring plan: q = ceil(count / n); chunk c = [c*q, min((c+1)*q, count)).
+    const uint64_t q = ceil_div(count, static_cast<uint64_t>(n));
+    const uint64_t epv = 16 / e;
+    const bool vec = all_aligned16(n, sendbufs, recvbufs) && (n == 1 || q % epv == 0);
+    DeviceGuard g(comm->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (comm->debug)
+        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%s q=%llu vec=%d\n", n, count,
+                     dtype_name(dtype), static_cast<int>(op), stepwise ? "stepwise" : "fused",
+                     static_cast<unsigned long long>(q), vec ? 1 : 0);
+
+    StepTimer timer(comm, stream);
+    hipError_t err = timer.begin(stepwise ? 2 * (n - 1) : 1);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+
+    if (!stepwise) {
+        ar::ReduceArgs a{};
+        fill_ptrs(a, n, sendbufs, recvbufs);
+        a.count = count;
+        a.q = q;
+        a.n = n;
+        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
+        err = ar::launch_fused_reduce(a, dtype, op, false, vec, gx, stream);
+        if (err != hipSuccess) return hip_fail(err, "fused all-reduce launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        timer.end();
+        return AR_SUCCESS;
+    }
+
+    // Reduce-scatter: n-1 steps. fp32/int32 partials travel in the recv
+    // buffers (as the ring adds into its own chunk views); fp16/bf16 partials
+    // stay in fp32 in the workspace, one slot per element.
+    ar::StepArgs sa{};
+    fill_ptrs(sa, n, sendbufs, recvbufs);
+    sa.ws = (dtype == AR_FLOAT16 || dtype == AR_BFLOAT16) ? comm->ws : nullptr;
+    sa.count = count;
+    sa.q = q;
+    sa.n = n;
+    sa.scatter = 0;
+    const int gx_rs = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
+    for (int s = 0; s < n - 1; ++s) {
+        sa.s = s;
+        sa.first = s == 0;
+        sa.last = s == n - 2;
+        err = ar::launch_rs_step(sa, dtype, op, vec, gx_rs, stream);
+        if (err != hipSuccess) return hip_fail(err, "reduce-scatter step launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    }
+    // All-gather: n-1 copy steps; step s moves chunk (r - s) mod n from rank r-1 to rank r.
+    ar::CopyArgs ca{};
+    for (int r = 0; r < n; ++r) ca.recv[r] = recvbufs[r];
+    ca.total = bytes;
+    ca.qb = q * e;
+    ca.n = n;
+    ca.shift = 0;
+    const bool cvec = all_aligned16(n, sendbufs, recvbufs) && (ca.qb % 16 == 0);
+    const int gx_ag = grid_for(comm, cvec ? ceil_div(ca.qb, 16) : ceil_div(ca.qb, 2), n);
+    for (int s = 0; s < n - 1; ++s) {
+        ca.s = s;
+        err = ar::launch_copy_step(ca, cvec, gx_ag, stream);
+        if (err != hipSuccess) return hip_fail(err, "all-gather step launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    }
+    timer.end();
+    return AR_SUCCESS;
+}
+
+AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
+                                        size_t recvcount, ar_dtype_t dtype, ar_op_t op, ar_mode_t mode,
+                                        hipStream_t stream)
+{
+    ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
+    if (rc != AR_SUCCESS) return rc;
+    if (!valid_op(op)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid op %d", static_cast<int>(op));
+    const int n = comm->nranks;
+    const size_t e = elem_size(dtype);
+    size_t rbytes = 0, total = 0, sbytes = 0;
+    if (!mul_ok(recvcount, e, &rbytes) || !mul_ok(recvcount, static_cast<size_t>(n), &total) || !mul_ok(total, e, &sbytes))
+        return fail(AR_ERR_INVALID_ARGUMENT, "recvcount %zu overflows", recvcount);
+    if (recvcount == 0) return AR_SUCCESS;
+    const bool stepwise = mode == AR_MODE_RING_STEPWISE && n > 1;
+    const size_t ws_need = stepwise ? ar_workspace_bytes(AR_COLL_REDUCE_SCATTER, n, recvcount, dtype, mode) : 0;
+    if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
+    rc = need_workspace(comm, ws_need);
+    if (rc != AR_SUCCESS) return rc;
+    rc = check_buffers(n, sendbufs, recvbufs, sbytes, rbytes, AR_COLL_REDUCE_SCATTER, e, comm->ws, ws_need);
+    if (rc != AR_SUCCESS) return rc;
+
+    const uint64_t q = recvcount;  // block c of the reduction is chunk c of the ring
+    const uint64_t epv = 16 / e;
+    const bool vec = all_aligned16(n, sendbufs, recvbufs) && q % epv == 0;
+    DeviceGuard g(comm->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (comm->debug)
+        std::fprintf(stderr, "[allreduce] reduce_scatter n=%d recvcount=%zu dtype=%s op=%d mode=%s vec=%d\n", n,
+                     recvcount, dtype_name(dtype), static_cast<int>(op), stepwise ? "stepwise" : "fused", vec ? 1 : 0);
+    StepTimer timer(comm, stream);
+    hipError_t err = timer.begin(stepwise ? n - 1 : 1);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+
+    if (!stepwise) {
+        ar::ReduceArgs a{};
+        fill_ptrs(a, n, sendbufs, recvbufs);
+        a.count = total;
+        a.q = q;
+        a.n = n;
+        err = ar::launch_fused_reduce(a, dtype, op, true, vec, grid_for(comm, vec ? ceil_div(q, epv) : q, n), stream);
+        if (err != hipSuccess) return hip_fail(err, "fused reduce-scatter launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        timer.end();
+        return AR_SUCCESS;
+    }
+    // The ring's reduce-scatter phase with partials in the workspace; the
+    // last step writes finished chunk c to recvbufs[c].
+    ar::StepArgs sa{};
+    fill_ptrs(sa, n, sendbufs, recvbufs);
+    sa.ws = comm->ws;
+    sa.count = total;
+    sa.q = q;
+    sa.n = n;
+    sa.scatter = 1;
+    const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
+    for (int s = 0; s < n - 1; ++s) {
+        sa.s = s;
+        sa.first = s == 0;
+        sa.last = s == n - 2;
+        err = ar::launch_rs_step(sa, dtype, op, vec, gx, stream);
+        if (err != hipSuccess) return hip_fail(err, "reduce-scatter step launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    }
+    timer.end();
+    return AR_SUCCESS;
+}
+
+AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
+                                    size_t sendcount, ar_dtype_t dtype, ar_mode_t mode, hipStream_t stream)
+{
+    ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
+    if (rc != AR_SUCCESS) return rc;
+    const int n = comm->nranks;
+    const size_t e = elem_size(dtype);
+    size_t blk = 0, rbytes = 0;
+    if (!mul_ok(sendcount, e, &blk) || !mul_ok(blk, static_cast<size_t>(n), &rbytes))
+        return fail(AR_ERR_INVALID_ARGUMENT, "sendcount %zu overflows", sendcount);
+    if (sendcount == 0) return AR_SUCCESS;
+    rc = check_buffers(n, sendbufs, recvbufs, blk, rbytes, AR_COLL_ALL_GATHER, e, nullptr, 0);
+    if (rc != AR_SUCCESS) return rc;
+    const bool stepwise = mode == AR_MODE_RING_STEPWISE && n > 1;
+    const bool vec = all_aligned16(n, sendbufs, recvbufs) && blk % 16 == 0;
+    DeviceGuard g(comm->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (comm->debug)
+        std::fprintf(stderr, "[allreduce] all_gather n=%d sendcount=%zu dtype=%s mode=%s vec=%d\n", n, sendcount,
+                     dtype_name(dtype), stepwise ? "stepwise" : "fused", vec ? 1 : 0);
+    StepTimer timer(comm, stream);
+    hipError_t err = timer.begin(stepwise ? n : 1);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+
+    if (!stepwise) {
+        ar::CopyArgs a{};
+        fill_ptrs(a, n, sendbufs, recvbufs);
+        a.total = blk;
+        a.n = n;
+        err = ar::launch_fused_gather(a, vec, grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n), stream);
+        if (err != hipSuccess) return hip_fail(err, "fused all-gather launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+        timer.end();
+        return AR_SUCCESS;
+    }
+    // Each rank first places its own block (unless in place), then n-1 ring
+    // steps: at step s rank r receives block (r - s - 1) mod n from rank r-1.
+    rc = local_copies(comm, n, sendbufs, recvbufs, blk, blk, stream);
+    if (rc != AR_SUCCESS) return rc;
+    if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    ar::CopyArgs ca{};
+    for (int r = 0; r < n; ++r) ca.recv[r] = recvbufs[r];
+    ca.total = rbytes;
+    ca.qb = blk;
+    ca.n = n;
+    ca.shift = 1;
+    const int gx = grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n);
+    for (int s = 0; s < n - 1; ++s) {
+        ca.s = s;
+        err = ar::launch_copy_step(ca, vec, gx, stream);
+        if (err != hipSuccess) return hip_fail(err, "all-gather step launch");
+        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    }
+    timer.end();
+    return AR_SUCCESS;
+}
+
+AR_EXPORT const char* ar_result_string(ar_result_t result)
+{
+    switch (result) {
+    case AR_SUCCESS: return "success";
+    case AR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case AR_ERR_UNSUPPORTED: return "unsupported";
+    case AR_ERR_HIP: return "HIP runtime error";
+    case AR_ERR_OUT_OF_MEMORY: return "out of memory";
+    case AR_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown result code";
+}
+
+AR_EXPORT const char* ar_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,72 @@
+// kernels.h -- internal interface between the C ABI (api.cpp) and the HIP
+// kernels (kernels.hip). Not installed; the public ABI is include/allreduce.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "allreduce.h"
+
+namespace ar {
+
+// Threads per workgroup for every kernel: four 64-wide wavefronts.
+constexpr int kBlock = 256;
+
+// Rank buffers and sizes of one reduction (all-reduce or reduce-scatter).
+//   count: elements per rank in the send buffers
+//   q:     chunk length; chunk c = [c*q, min((c+1)*q, count))
+struct ReduceArgs {
+    const void* send[AR_MAX_RANKS];
+    void* recv[AR_MAX_RANKS];
+    uint64_t count;
+    uint64_t q;
+    int n;
+};
+
+// One ring reduce-scatter step. Chunk (r - s - 1) mod n is combined at rank r:
+// local (send[r]) (+) incoming (send[left] on the first step, else the
+// partial kept in recv[left] or in the fp32/uint32 workspace ws).
+struct StepArgs {
+    const void* send[AR_MAX_RANKS];
+    void* recv[AR_MAX_RANKS];
+    void* ws;          // accumulator workspace (count slots of 4 bytes) or null
+    uint64_t count;
+    uint64_t q;
+    int n;
+    int s;             // step index, 0..n-2
+    int first;         // s == 0
+    int last;          // s == n-2: finalize (AVG, rounding) and write the result
+    int scatter;       // reduce-scatter layout: finished chunk c goes to recv[c]
+};
+
+// Byte copies between rank buffers. Copy step s of a ring: chunk
+// (r - s - shift) mod n of recv[left] goes to the same place in recv[r].
+// Chunk c spans bytes [c*qb, min((c+1)*qb, total)). For a local copy
+// (shift < 0): send[r] -> recv[r] + r*dst_stride bytes, `total` bytes each.
+struct CopyArgs {
+    const void* send[AR_MAX_RANKS];
+    void* recv[AR_MAX_RANKS];
+    uint64_t total;    // bytes per rank buffer covered by the chunks
+    uint64_t qb;       // chunk length in bytes
+    uint64_t dst_stride;
+    int n;
+    int s;
+    int shift;
+};
+
+// Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
+// has checked alignment and q % (16/elem) == 0).
+hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec,
+                               int grid_x, hipStream_t stream);
+
+// Fused all-gather: block p of send[p] (blk bytes) to recv[r] + p*blk for all r.
+hipError_t launch_fused_gather(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);
+
+hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x, hipStream_t stream);
+
+hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);
+
+// send[r] -> recv[r] + r*dst_stride, total bytes, for every rank.
+hipError_t launch_local_copy(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);
+
+}  // namespace ar

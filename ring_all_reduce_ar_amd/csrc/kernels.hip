@@ -1,0 +1,637 @@
+// kernels.hip -- HIP kernels of the ring all-reduce for CDNA4 (gfx950).
+//
+// The reduction is elementwise and HBM-bound: one combine per element and
+// rank against 2*sizeof(T) bytes moved, far below any matrix-core ridge, so
+// there is no MFMA here. What matters is moving bytes: 16-byte (dwordx4)
+// loads and non-temporal stores, one wavefront-uniform chunk per workgroup
+// row so the rank order of the fold is a scalar (SGPR) choice, and enough
+// loads in flight per CU.
+//
+// Ring order [geek-doc "训练梯度同步与集合通信", section 三; handbook
+// "集合通信原语", section 环形 all-reduce 与通信量]: chunk c of the buffer is
+// reduced by the ring as acc = x_c, then acc = x_{c+k} (+) acc for
+// k = 1..n-1 (ranks mod n). Every kernel below folds in exactly that order,
+// so the fused and stepwise modes give the same bits.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace ar {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// element formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+__device__ __forceinline__ float half_to_f32(uint32_t h)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// v_cvt_f16_f32: round to nearest even (the default mode), subnormals kept.
+__device__ __forceinline__ uint32_t f32_to_half(float f)
+{
+    if (__builtin_isnan(f)) return ((as_u(f) >> 16) & 0x8000u) | 0x7E00u;
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return as_f(b << 16); }
+
+// bfloat16 keeps the top 16 bits of the fp32 pattern; adding 0x7FFF plus the
+// lowest kept bit rounds the dropped 16 bits to nearest, ties to even (a
+// carry into the exponent is the correct rounding up, up to infinity).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = as_u(f);
+    if (__builtin_isnan(f)) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+struct F32 {
+    using Acc = float;
+    static constexpr int kEpv = 4;  // elements per 16-byte vector
+    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return static_cast<const float*>(p)[i]; }
+    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { static_cast<float*>(p)[i] = v; }
+    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
+    {
+        a[0] = as_f(v.x); a[1] = as_f(v.y); a[2] = as_f(v.z); a[3] = as_f(v.w);
+    }
+    static __device__ __forceinline__ u32x4 pack(const Acc* a)
+    {
+        return u32x4{as_u(a[0]), as_u(a[1]), as_u(a[2]), as_u(a[3])};
+    }
+};
+
+struct I32 {
+    using Acc = uint32_t;  // two's-complement wrap
+    static constexpr int kEpv = 4;
+    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return static_cast<const uint32_t*>(p)[i]; }
+    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { static_cast<uint32_t*>(p)[i] = v; }
+    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a) { a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w; }
+    static __device__ __forceinline__ u32x4 pack(const Acc* a) { return u32x4{a[0], a[1], a[2], a[3]}; }
+};
+
+struct F16 {
+    using Acc = float;
+    static constexpr int kEpv = 8;
+    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i)
+    {
+        return half_to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v)
+    {
+        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_half(v));
+    }
+    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[2 * j] = half_to_f32(w[j] & 0xFFFFu);
+            a[2 * j + 1] = half_to_f32(w[j] >> 16);
+        }
+    }
+    static __device__ __forceinline__ u32x4 pack(const Acc* a)
+    {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = f32_to_half(a[2 * j]) | (f32_to_half(a[2 * j + 1]) << 16);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+struct BF16 {
+    using Acc = float;
+    static constexpr int kEpv = 8;
+    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i)
+    {
+        return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v)
+    {
+        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
+    }
+    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[2 * j] = as_f(w[j] << 16);
+            a[2 * j + 1] = as_f(w[j] & 0xFFFF0000u);
+        }
+    }
+    static __device__ __forceinline__ u32x4 pack(const Acc* a)
+    {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16(a[2 * j]) | (f32_to_bf16(a[2 * j + 1]) << 16);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+// ---------------------------------------------------------------------------
+// reduce ops: local (+) incoming [mhpq.cn all-reduce article, section 2.1]
+// ---------------------------------------------------------------------------
+// MAX/MIN: NaN if either operand is NaN; equal operands (including +0/-0)
+// combine their sign bits so that +0 > -0 and the op is commutative.
+__device__ __forceinline__ float fp_max(float a, float b)
+{
+    if (__builtin_isnan(a) || __builtin_isnan(b)) return as_f(0x7FC00000u);
+    if (a == b) return as_f(as_u(a) & as_u(b));
+    return a > b ? a : b;
+}
+
+__device__ __forceinline__ float fp_min(float a, float b)
+{
+    if (__builtin_isnan(a) || __builtin_isnan(b)) return as_f(0x7FC00000u);
+    if (a == b) return as_f(as_u(a) | as_u(b));
+    return a < b ? a : b;
+}
+
+template <int OP>
+__device__ __forceinline__ float combine(float local, float in)
+{
+    if constexpr (OP == AR_SUM || OP == AR_AVG) return local + in;
+    else if constexpr (OP == AR_PROD) return local * in;
+    else if constexpr (OP == AR_MAX) return fp_max(local, in);
+    else return fp_min(local, in);
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t combine(uint32_t local, uint32_t in)
+{
+    if constexpr (OP == AR_SUM || OP == AR_AVG) return local + in;
+    else if constexpr (OP == AR_PROD) return local * in;
+    else if constexpr (OP == AR_MAX) return static_cast<int32_t>(local) > static_cast<int32_t>(in) ? local : in;
+    else return static_cast<int32_t>(local) < static_cast<int32_t>(in) ? local : in;
+}
+
+// AVG: the finished sum divided once by n (correctly rounded fp32 divide;
+// int32 truncates toward zero).
+template <int OP>
+__device__ __forceinline__ float finalize(float a, int n)
+{
+    if constexpr (OP == AR_AVG) return a / static_cast<float>(n);
+    else return a;
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t finalize(uint32_t a, int n)
+{
+    if constexpr (OP == AR_AVG) return static_cast<uint32_t>(static_cast<int32_t>(a) / n);
+    else return a;
+}
+
+// ---------------------------------------------------------------------------
+// memory access
+// ---------------------------------------------------------------------------
+// Streaming loads/stores: each input is read once and each output written
+// once, so both bypass cache retention (nt).
+__device__ __forceinline__ u32x4 ld16_nt(const void* base, uint64_t v)
+{
+    return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + v);
+}
+__device__ __forceinline__ void st16_nt(void* base, uint64_t v, u32x4 x)
+{
+    __builtin_nontemporal_store(x, static_cast<u32x4*>(base) + v);
+}
+__device__ __forceinline__ u32x4 ld16(const void* base, uint64_t v) { return static_cast<const u32x4*>(base)[v]; }
+__device__ __forceinline__ void st16(void* base, uint64_t v, u32x4 x) { static_cast<u32x4*>(base)[v] = x; }
+
+__device__ __forceinline__ int wrap_rank(int r, int n) { return r >= n ? r - n : r; }
+
+__device__ __forceinline__ void chunk_range(uint64_t q, uint64_t count, int c, uint64_t& lo, uint64_t& hi)
+{
+    lo = min(static_cast<uint64_t>(c) * q, count);
+    hi = min(lo + q, count);
+}
+
+// ---------------------------------------------------------------------------
+// fused single-pass reduction
+// ---------------------------------------------------------------------------
+// Element i of chunk c, all ranks, in ring order.
+template <class F, int OP>
+__device__ __forceinline__ typename F::Acc fold_elem(const ReduceArgs& a, int c, int n, uint64_t i)
+{
+    typename F::Acc acc = F::ld(a.send[c], i);
+    for (int k = 1; k < n; ++k) acc = combine<OP>(F::ld(a.send[wrap_rank(c + k, n)], i), acc);
+    return acc;
+}
+
+// Vector vi (16 bytes) of chunk c, all ranks, in ring order. NR > 0 fixes the
+// rank count at compile time (all NR loads issued before the first combine);
+// NR == 0 takes it from the arguments and loads in batches of 8.
+template <class F, int OP, int NR>
+__device__ __forceinline__ void fold_vec(const ReduceArgs& a, int c, int n, uint64_t vi, typename F::Acc* acc)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    if constexpr (NR > 0) {
+        u32x4 x[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) x[k] = ld16_nt(a.send[wrap_rank(c + k, NR)], vi);
+        F::unpack(x[0], acc);
+#pragma unroll
+        for (int k = 1; k < NR; ++k) {
+            Acc t[E];
+            F::unpack(x[k], t);
+#pragma unroll
+            for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
+        }
+    } else {
+        F::unpack(ld16_nt(a.send[c], vi), acc);
+        for (int k = 1; k < n; k += 8) {
+            const int b = min(8, n - k);
+            u32x4 x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < b) x[j] = ld16_nt(a.send[wrap_rank(c + k + j, n)], vi);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < b) {
+                    Acc t[E];
+                    F::unpack(x[j], t);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] = combine<OP>(t[e], acc[e]);
+                }
+            }
+        }
+    }
+}
+
+// grid = (blocks per chunk, n chunks). Workgroup row y handles chunk y, so the
+// ring order (which rank's buffer is loaded k-th) is uniform per workgroup.
+// All-reduce (SCATTER = false) writes the result to every rank; reduce-scatter
+// (SCATTER = true) writes chunk c to recv[c] only. Every input element is read
+// before any output of the same element is written, by the same thread, so
+// send and recv may be the same buffers.
+template <class F, int OP, int NR, bool SCATTER>
+__global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const int n = NR > 0 ? NR : a.n;
+    const int c = blockIdx.y;
+    uint64_t lo, hi;
+    chunk_range(a.q, a.count, c, lo, hi);
+    const uint64_t nv = (hi - lo) / E;
+    const uint64_t v0 = lo / E;  // exact: the host requires q % E == 0
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t v = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; v < nv; v += stride) {
+        Acc acc[E];
+        fold_vec<F, OP, NR>(a, c, n, v0 + v, acc);
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
+        const u32x4 out = F::pack(acc);
+        if constexpr (SCATTER) {
+            st16_nt(a.recv[c], v, out);
+        } else {
+#pragma unroll
+            for (int r = 0; r < n; ++r) st16_nt(a.recv[r], v0 + v, out);
+        }
+    }
+    // A chunk whose length is not a whole number of vectors (only the last
+    // non-empty one) finishes its < E trailing elements here.
+    if (blockIdx.x == 0) {
+        const uint64_t i = lo + nv * E + threadIdx.x;
+        if (i < hi) {
+            const Acc x = finalize<OP>(fold_elem<F, OP>(a, c, n, i), n);
+            if constexpr (SCATTER) {
+                F::st(a.recv[c], i - lo, x);
+            } else {
+                for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
+            }
+        }
+    }
+}
+
+// Element-wise variant for buffers that are not 16-byte aligned or chunks that
+// do not start on a vector boundary.
+template <class F, int OP, bool SCATTER>
+__global__ __launch_bounds__(kBlock) void fused_reduce_scalar(const ReduceArgs a)
+{
+    const int n = a.n;
+    const int c = blockIdx.y;
+    uint64_t lo, hi;
+    chunk_range(a.q, a.count, c, lo, hi);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = lo + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < hi; i += stride) {
+        const typename F::Acc x = finalize<OP>(fold_elem<F, OP>(a, c, n, i), n);
+        if constexpr (SCATTER) {
+            F::st(a.recv[c], i - lo, x);
+        } else {
+            for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fused all-gather: block p of send[p] -> recv[r] + p*blk for every r
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void fused_gather(const CopyArgs a)
+{
+    const int p = blockIdx.y;
+    const uint64_t blk = a.total;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if constexpr (VEC) {
+        const uint64_t nv = blk / 16, o = p * blk / 16;
+        for (uint64_t v = t0; v < nv; v += stride) {
+            const u32x4 x = ld16_nt(a.send[p], v);
+            for (int r = 0; r < a.n; ++r) st16_nt(a.recv[r], o + v, x);
+        }
+    } else {
+        const uint64_t nh = blk / 2, o = p * blk / 2;
+        const uint16_t* src = static_cast<const uint16_t*>(a.send[p]);
+        for (uint64_t h = t0; h < nh; h += stride) {
+            const uint16_t x = src[h];
+            for (int r = 0; r < a.n; ++r) static_cast<uint16_t*>(a.recv[r])[o + h] = x;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ring-stepwise mode
+// ---------------------------------------------------------------------------
+// Accumulator slots in the workspace are 32-bit patterns. The conversions
+// take their operand by value: bit-casting a vector element in place (w.y)
+// is compiled as a read of the vector's first element.
+__device__ __forceinline__ void from_bits(uint32_t u, float& out) { out = as_f(u); }
+__device__ __forceinline__ void from_bits(uint32_t u, uint32_t& out) { out = u; }
+__device__ __forceinline__ uint32_t to_bits(float v) { return as_u(v); }
+__device__ __forceinline__ uint32_t to_bits(uint32_t v) { return v; }
+
+template <class F>
+__device__ __forceinline__ void ws_load(const void* ws, uint64_t i, typename F::Acc* acc)
+{
+    constexpr int E = F::kEpv;
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+        const u32x4 w = ld16(ws, i / 4 + j);
+        from_bits(w.x, acc[4 * j + 0]);
+        from_bits(w.y, acc[4 * j + 1]);
+        from_bits(w.z, acc[4 * j + 2]);
+        from_bits(w.w, acc[4 * j + 3]);
+    }
+}
+
+template <class F>
+__device__ __forceinline__ void ws_store(void* ws, uint64_t i, const typename F::Acc* acc)
+{
+    constexpr int E = F::kEpv;
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+        const u32x4 w{to_bits(acc[4 * j + 0]), to_bits(acc[4 * j + 1]), to_bits(acc[4 * j + 2]),
+                      to_bits(acc[4 * j + 3])};
+        st16(ws, i / 4 + j, w);
+    }
+}
+
+// One element of a reduce-scatter step at rank r (chunk c, left neighbour).
+template <class F, int OP>
+__device__ __forceinline__ void rs_elem(const StepArgs& a, int r, int left, int c, uint64_t lo, uint64_t i)
+{
+    using Acc = typename F::Acc;
+    const Acc local = F::ld(a.send[r], i);
+    Acc in;
+    if (a.first) in = F::ld(a.send[left], i);
+    else if (a.ws) from_bits(static_cast<const uint32_t*>(a.ws)[i], in);
+    else in = F::ld(a.recv[left], i);
+    Acc v = combine<OP>(local, in);
+    if (a.last) {
+        v = finalize<OP>(v, a.n);
+        if (a.scatter) F::st(a.recv[c], i - lo, v);
+        else F::st(a.recv[r], i, v);
+    } else if (a.ws) {
+        static_cast<uint32_t*>(a.ws)[i] = to_bits(v);
+    } else {
+        F::st(a.recv[r], i, v);
+    }
+}
+
+// Reduce-scatter step s [handbook "集合通信原语", section 环形 all-reduce 与通信量]:
+// every rank r combines chunk (r - s - 1) mod n of its own input with the
+// partial arriving from rank r-1. grid = (blocks, n ranks). The chunks a step
+// writes (rank r, chunk c) and reads from the left (rank r-1, chunk c) are
+// disjoint from what rank r-1 writes in the same step (its chunk c-1), so no
+// staging buffer is needed.
+template <class F, int OP, bool VEC>
+__global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const int n = a.n;
+    const int r = blockIdx.y;
+    const int left = r == 0 ? n - 1 : r - 1;
+    int c = (r - a.s - 1) % n;
+    if (c < 0) c += n;
+    uint64_t lo, hi;
+    chunk_range(a.q, a.count, c, lo, hi);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    uint64_t done = lo;
+    if constexpr (VEC) {
+        const uint64_t nv = (hi - lo) / E, v0 = lo / E;
+        for (uint64_t v = t0; v < nv; v += stride) {
+            const uint64_t vi = v0 + v;
+            Acc loc[E], in[E];
+            F::unpack(ld16(a.send[r], vi), loc);
+            if (a.first) F::unpack(ld16(a.send[left], vi), in);
+            else if (a.ws) ws_load<F>(a.ws, vi * E, in);
+            else F::unpack(ld16(a.recv[left], vi), in);
+#pragma unroll
+            for (int j = 0; j < E; ++j) loc[j] = combine<OP>(loc[j], in[j]);
+            if (a.last) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) loc[j] = finalize<OP>(loc[j], n);
+                if (a.scatter) st16(a.recv[c], v, F::pack(loc));
+                else st16(a.recv[r], vi, F::pack(loc));
+            } else if (a.ws) {
+                ws_store<F>(a.ws, vi * E, loc);
+            } else {
+                st16(a.recv[r], vi, F::pack(loc));
+            }
+        }
+        done = lo + nv * E;
+        if (blockIdx.x == 0 && done + threadIdx.x < hi) rs_elem<F, OP>(a, r, left, c, lo, done + threadIdx.x);
+    } else {
+        for (uint64_t i = lo + t0; i < hi; i += stride) rs_elem<F, OP>(a, r, left, c, lo, i);
+    }
+}
+
+// Copy step s of a ring: rank r copies chunk (r - s - shift) mod n from rank
+// r-1 (all-gather phase [handbook, section 环形 all-reduce 与通信量]).
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void copy_step(const CopyArgs a)
+{
+    const int n = a.n;
+    const int r = blockIdx.y;
+    const int left = r == 0 ? n - 1 : r - 1;
+    int c = (r - a.s - a.shift) % n;
+    if (c < 0) c += n;
+    uint64_t lo, hi;
+    chunk_range(a.qb, a.total, c, lo, hi);
+    const char* src = static_cast<const char*>(a.recv[left]);
+    char* dst = static_cast<char*>(a.recv[r]);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    uint64_t done = lo;
+    if constexpr (VEC) {
+        const uint64_t nv = (hi - lo) / 16, v0 = lo / 16;
+        for (uint64_t v = t0; v < nv; v += stride) st16(dst, v0 + v, ld16(src, v0 + v));
+        done = lo + nv * 16;
+        if (blockIdx.x != 0) return;
+        for (uint64_t b = done + 2 * threadIdx.x; b < hi; b += 2 * kBlock)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    } else {
+        for (uint64_t b = done + 2 * t0; b < hi; b += 2 * stride)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    }
+}
+
+// send[r] -> recv[r] + r*dst_stride, `total` bytes per rank.
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void local_copy(const CopyArgs a)
+{
+    const int r = blockIdx.y;
+    const char* src = static_cast<const char*>(a.send[r]);
+    char* dst = static_cast<char*>(a.recv[r]) + static_cast<uint64_t>(r) * a.dst_stride;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    uint64_t done = 0;
+    if constexpr (VEC) {
+        const uint64_t nv = a.total / 16;
+        for (uint64_t v = t0; v < nv; v += stride) st16(dst, v, ld16(src, v));
+        done = nv * 16;
+        if (blockIdx.x != 0) return;
+        for (uint64_t b = done + 2 * threadIdx.x; b < a.total; b += 2 * kBlock)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    } else {
+        for (uint64_t b = 2 * t0; b < a.total; b += 2 * stride)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <class F, int OP, bool SC>
+hipError_t fused_n(const ReduceArgs& a, bool vec, dim3 grid, hipStream_t s)
+{
+    const dim3 block(kBlock);
+    if (!vec) {
+        hipLaunchKernelGGL((fused_reduce_scalar<F, OP, SC>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    switch (a.n) {
+    case 2: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 2, SC>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 3, SC>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 4, SC>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC>), grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <class F, bool SC>
+hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+{
+    switch (op) {
+    case AR_SUM: return fused_n<F, AR_SUM, SC>(a, vec, grid, s);
+    case AR_AVG: return fused_n<F, AR_AVG, SC>(a, vec, grid, s);
+    case AR_MAX: return fused_n<F, AR_MAX, SC>(a, vec, grid, s);
+    case AR_MIN: return fused_n<F, AR_MIN, SC>(a, vec, grid, s);
+    case AR_PROD: return fused_n<F, AR_PROD, SC>(a, vec, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool SC>
+hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+{
+    switch (dtype) {
+    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, grid, s);
+    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, grid, s);
+    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, grid, s);
+    case AR_INT32: return fused_op<I32, SC>(a, op, vec, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class F, int OP>
+hipError_t rs_vec(const StepArgs& a, bool vec, dim3 grid, hipStream_t s)
+{
+    if (vec) hipLaunchKernelGGL((rs_step<F, OP, true>), grid, dim3(kBlock), 0, s, a);
+    else hipLaunchKernelGGL((rs_step<F, OP, false>), grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class F>
+hipError_t rs_op(const StepArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+{
+    switch (op) {
+    case AR_SUM: return rs_vec<F, AR_SUM>(a, vec, grid, s);
+    case AR_AVG: return rs_vec<F, AR_AVG>(a, vec, grid, s);
+    case AR_MAX: return rs_vec<F, AR_MAX>(a, vec, grid, s);
+    case AR_MIN: return rs_vec<F, AR_MIN>(a, vec, grid, s);
+    case AR_PROD: return rs_vec<F, AR_PROD>(a, vec, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, int grid_x,
+                               hipStream_t stream)
+{
+    const dim3 grid(grid_x, a.n);
+    return scatter ? fused_dtype<true>(a, dtype, op, vec, grid, stream)
+                   : fused_dtype<false>(a, dtype, op, vec, grid, stream);
+}
+
+hipError_t launch_fused_gather(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream)
+{
+    const dim3 grid(grid_x, a.n);
+    if (vec) hipLaunchKernelGGL((fused_gather<true>), grid, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((fused_gather<false>), grid, dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x, hipStream_t stream)
+{
+    const dim3 grid(grid_x, a.n);
+    switch (dtype) {
+    case AR_FLOAT32: return rs_op<F32>(a, op, vec, grid, stream);
+    case AR_FLOAT16: return rs_op<F16>(a, op, vec, grid, stream);
+    case AR_BFLOAT16: return rs_op<BF16>(a, op, vec, grid, stream);
+    case AR_INT32: return rs_op<I32>(a, op, vec, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream)
+{
+    const dim3 grid(grid_x, a.n);
+    if (vec) hipLaunchKernelGGL((copy_step<true>), grid, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((copy_step<false>), grid, dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_local_copy(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream)
+{
+    const dim3 grid(grid_x, a.n);
+    if (vec) hipLaunchKernelGGL((local_copy<true>), grid, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((local_copy<false>), grid, dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ar

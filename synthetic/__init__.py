@@ -52,16 +52,17 @@ def _fill(out: torch.Tensor, draw):
     return out
 
 
-def uniform(count: int, lo: float, hi: float, gen: torch.Generator, dtype=torch.float32, device="cpu"):
-    """uniform[lo, hi) drawn in fp32, rounded to ``dtype``."""
-    out = torch.empty(count, dtype=dtype, device=device)
+def uniform(count: int, lo: float, hi: float, gen: torch.Generator, dtype=torch.float32, device="cpu", out=None):
+    """uniform[lo, hi) drawn in fp32, rounded to ``dtype`` (into ``out`` if given)."""
+    if out is None:
+        out = torch.empty(count, dtype=dtype, device=device)
     return _fill(out, lambda n: torch.empty(n, dtype=torch.float32, device=device).uniform_(lo, hi, generator=gen))
 
 
 def gaussian(count: int, std: float, gen: torch.Generator, dtype=torch.float32, device="cpu",
-             outlier_frac: float = 0.0, outlier_std: float = 1.0):
+             outlier_frac: float = 0.0, outlier_std: float = 1.0, out=None):
     """N(0, std^2) drawn in fp32; with probability ``outlier_frac`` an element is
-    drawn from N(0, outlier_std^2) instead. Rounded to ``dtype``."""
+    drawn from N(0, outlier_std^2) instead. Rounded to ``dtype`` (into ``out`` if given)."""
     def draw(n):
         x = torch.randn(n, dtype=torch.float32, device=device, generator=gen) * std
         if outlier_frac > 0:
@@ -69,7 +70,8 @@ def gaussian(count: int, std: float, gen: torch.Generator, dtype=torch.float32, 
             big = torch.randn(n, dtype=torch.float32, device=device, generator=gen) * outlier_std
             x = torch.where(pick, big, x)
         return x
-    out = torch.empty(count, dtype=dtype, device=device)
+    if out is None:
+        out = torch.empty(count, dtype=dtype, device=device)
     return _fill(out, draw)
 
 

@@ -1,0 +1,129 @@
+"""Parity at the workloads' full sizes, in place, as the benchmark launches
+them. Where host memory or oracle time allows, every element is compared;
+otherwise sampled elements (random ones plus every chunk boundary and the
+ends) are computed one by one by the oracle from host copies of their
+inputs taken before the call, and two properties are checked on the whole
+buffers on the device: every rank holds the same result, and nothing
+outside the payload changed (guard bands of the comparison tests cover that
+at small sizes)."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import oracle
+import ring_all_reduce_ar_amd as ar
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_indices(n, count, rng, m=20000):
+    q = -(-count // n)
+    idx = set(rng.integers(0, count, size=m).tolist())
+    for c in range(n + 1):
+        for d in (-2, -1, 0, 1, 2):
+            i = c * q + d
+            if 0 <= i < count:
+                idx.add(i)
+    idx.update({0, count - 1})
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def gather(bufs, idx):
+    it = torch.from_numpy(idx).to(bufs[0].device)
+    vals = torch.stack([b[it] for b in bufs], dim=1).contiguous()
+    return synthetic.to_numpy(vals.view(-1)).reshape(vals.shape)
+
+
+def check_sampled(comm, bufs, dtype, op, mode, seed=0):
+    """In-place all-reduce of bufs, checked at sampled elements and for
+    identical ranks."""
+    n, count = len(bufs), bufs[0].numel()
+    idx = sample_indices(n, count, np.random.default_rng(seed))
+    before = gather(bufs, idx)
+    exp = oracle.all_reduce_elements(before, idx, count, dtype, op)
+    ptrs = [b.data_ptr() for b in bufs]
+    ar.ar_all_reduce(comm, ptrs, ptrs, count, dtype, op, mode)
+    torch.cuda.synchronize()
+    after = gather(bufs, idx)
+    for r in range(n):
+        gu.assert_same(np.ascontiguousarray(after[:, r]), exp, dtype, f"{mode} {dtype} {op} rank {r} sampled")
+    for r in range(1, n):
+        assert torch.equal(bufs[r].view(torch.uint8), bufs[0].view(torch.uint8)), f"rank {r} differs from rank 0"
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+def test_bucket25_avg_full_compare(mode):
+    """8 ranks x one 25 MiB fp32 DDP bucket, N(0, 1e-3^2), AVG: every element."""
+    n, count = 8, 6_553_600
+    with ar.Comm(n, 0) as comm:
+        xs = synthetic.rank_inputs("bucket25", n, count, "f32", device="cuda")
+        exp = oracle.fold_all_reduce([gu.host(x) for x in xs], "f32", "avg")
+        ptrs = [x.data_ptr() for x in xs]
+        ar.ar_all_reduce(comm, ptrs, ptrs, count, "f32", "avg", mode)
+        torch.cuda.synchronize()
+        for r in range(n):
+            gu.assert_same(gu.host(xs[r]), exp[r], "f32", f"bucket25 {mode} rank {r}")
+    del xs
+    free()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "i32"])
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+def test_sweep_sizes(mode, dtype):
+    """8 ranks, 1 KiB .. 256 MiB per rank in powers of two, SUM; every
+    element up to 16 MiB, sampled above."""
+    n = 8
+    with ar.Comm(n, 0) as comm:
+        for log2 in range(10, 29):
+            count = (1 << log2) // 4
+            xs = synthetic.rank_inputs("sweep", n, count, dtype, device="cuda", salt=log2)
+            if log2 <= 24:
+                exp = oracle.fold_all_reduce([gu.host(x) for x in xs], dtype, "sum")
+                ptrs = [x.data_ptr() for x in xs]
+                ar.ar_all_reduce(comm, ptrs, ptrs, count, dtype, "sum", mode)
+                torch.cuda.synchronize()
+                for r in range(n):
+                    gu.assert_same(gu.host(xs[r]), exp[r], dtype, f"sweep 2^{log2} B {mode} rank {r}")
+            else:
+                check_sampled(comm, xs, dtype, "sum", mode, seed=log2)
+            del xs
+    free()
+
+
+def test_grad7b_fp16_avg():
+    """8 ranks x 7e9 fp16 (14 GB each), N(0, 1e-3^2) with 1% N(0, 1)
+    outliers, AVG with fp32 accumulation, in place: fused (the benchmark's
+    launch), then stepwise on fresh inputs with its 28 GB fp32 workspace."""
+    n, count = 8, 7_000_000_000
+    with ar.Comm(n, 0) as comm:
+        bufs = synthetic.rank_inputs("grad7b", n, count, "f16", device="cuda")
+        check_sampled(comm, bufs, "f16", "avg", "fused", seed=4)
+        for r, b in enumerate(bufs):
+            synthetic.gaussian(count, 1e-3, synthetic.generator("grad7b", r, "cuda", salt=1), torch.float16,
+                               "cuda", outlier_frac=0.01, out=b)
+        ws = gu.attach_workspace(comm, ar.AR_COLL_ALL_REDUCE, n, count, "f16", "stepwise")
+        check_sampled(comm, bufs, "f16", "avg", "stepwise", seed=5)
+        ar.ar_comm_set_workspace(comm, None)
+        del ws
+    del bufs
+    free()
+
+
+@pytest.mark.parametrize("op", ["max", "min", "prod"])
+def test_bucket64_ops(op):
+    """64 ranks x 64M fp32 (256 MiB each), MAX/MIN on uniform[-1, 1), PROD on
+    uniform[0.99, 1.01), fused and stepwise."""
+    n, count = 64, 67_108_864
+    with ar.Comm(n, 0) as comm:
+        for mode, salt in (("fused", 0), ("stepwise", 1)):
+            bufs = synthetic.rank_inputs("bucket64", n, count, "f32", device="cuda", op=op, salt=salt)
+            check_sampled(comm, bufs, "f32", op, mode, seed=salt)
+            del bufs
+            free()
