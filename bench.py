@@ -93,6 +93,33 @@ def cpu_baseline(nranks: int, dtype: str, op: str, workload: str):
             "seconds": dt}
 
 
+def copy_probe(args, torch, ar):
+    """Plain copy of a known size: src read once, dst written once."""
+    nbytes = args.copy_probe
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    comm = ar.Comm(1, 0)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ar.ar_all_gather(comm, [src.data_ptr()], [dst.data_ptr()], nbytes // 4, "i32", "fused", stream)
+
+    for _ in range(args.warmup):
+        step()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    assert torch.equal(src, dst)
+    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"probe": "copy", "bytes": nbytes, "ms_per_copy": round(ms, 4), "hbm_gbps": round(gbps, 1),
+                      "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": args.steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +128,10 @@ def main():
     ap.add_argument("--workload", default="grad7b", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="instead of the all-reduce, time a plain 16-byte-vector device copy of BYTES bytes "
+                         "(a one-rank all-gather): the practical HBM ceiling, and the reference reading for "
+                         "the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -116,6 +147,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args, torch, ar)
+        return
     n, count, dtype, op, desc = WORKLOADS[args.workload]
     wl = args.workload if args.workload in synthetic.WORKLOAD_IDS else "sweep"
     print(f"[bench] generating {desc}", file=sys.stderr, flush=True)
