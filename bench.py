@@ -56,6 +56,25 @@ ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4}
 CPU_WINDOW_LOG2 = 26  # elements per rank in the CPU oracle's window
 
 
+def alpha_beta_time(nranks: int, msg_bytes: float, alpha_s: float, beta_bytes_per_s: float):
+    """Ring all-reduce time in the alpha-beta model (geek-doc page "训练梯度同步
+    与集合通信", section 四; handbook "集合通信原语", section α-β 模型):
+    T = 2(N-1)*alpha + 2(N-1)/N * M / beta. Returns (latency term, bandwidth
+    term, total) in seconds."""
+    lat = 2 * (nranks - 1) * alpha_s
+    bw = 2 * (nranks - 1) / nranks * msg_bytes / beta_bytes_per_s
+    return lat, bw, lat + bw
+
+
+def fit_line(xs, ys):
+    """Least-squares y = a + b*x; returns (a, b)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx if sxx else 0.0
+    return my - b * mx, b
+
+
 def kernel_sha() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -120,14 +139,74 @@ def copy_probe(args, torch, ar):
                       "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": args.steps}), flush=True)
 
 
+def sweep(args, torch, ar, synthetic):
+    """The alpha vs beta regimes: 8 ranks, 1 KiB .. 256 MiB per rank in powers
+    of two, fp32 SUM, in place, each mode. One JSON line per (mode, size),
+    then one line with the least-squares fits
+      ring modes: T = 2(N-1)*alpha + moved/beta, moved = 5(N-1)*S (the bytes
+                  the N-1 reduce-scatter and N-1 all-gather steps move)
+      fused:      T = alpha + 2*N*S/beta."""
+    n = 8
+    rows = []
+    with ar.Comm(n, 0) as comm:
+        for log2 in range(10, 29):
+            s_bytes = 1 << log2
+            count = s_bytes // 4
+            bufs = synthetic.rank_inputs("sweep", n, count, "f32", device="cuda", salt=log2)
+            ptrs = [b.data_ptr() for b in bufs]
+            stream = torch.cuda.current_stream()
+            for mode in ("fused", "stepwise", "graph"):
+                def call():
+                    ar.ar_all_reduce(comm, ptrs, ptrs, count, "f32", "sum", mode, stream)
+                for _ in range(5):
+                    call()
+                iters = max(20, min(2000, int(2e9 / (2 * n * s_bytes))))
+                start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                start.record(stream)
+                for _ in range(iters):
+                    call()
+                stop.record(stream)
+                torch.cuda.synchronize()
+                ms = start.elapsed_time(stop) / iters
+                moved = 2 * n * s_bytes if mode == "fused" else 5 * (n - 1) * s_bytes
+                row = {"sweep": mode, "bytes_per_rank": s_bytes, "us": round(ms * 1e3, 3), "iters": iters,
+                       "algbw_gbps": round(s_bytes / (ms * 1e-3) / 1e9, 3),
+                       "busbw_gbps": round(s_bytes / (ms * 1e-3) / 1e9 * 2 * (n - 1) / n, 3),
+                       "moved_bytes": moved, "moved_gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
+                if mode == "stepwise":
+                    ar.ar_comm_set_step_timing(comm, True)
+                    call()
+                    steps = ar.ar_last_step_times_ms(comm)
+                    ar.ar_comm_set_step_timing(comm, False)
+                    row["step_us"] = [round(t * 1e3, 2) for t in steps]
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+            del bufs
+            torch.cuda.empty_cache()
+    fits = {}
+    for mode in ("fused", "stepwise", "graph"):
+        rs = [r for r in rows if r["sweep"] == mode]
+        a, b = fit_line([r["moved_bytes"] for r in rs], [r["us"] * 1e-6 for r in rs])
+        launches = 1 if mode == "fused" else 2 * (n - 1)
+        fits[mode] = {"alpha_us": round(a / launches * 1e6, 3), "beta_gbps": round(1 / b / 1e9, 1) if b > 0 else None,
+                      "model": "T = %d*alpha + moved/beta" % launches}
+    small = {m: min(r["us"] for r in rows if r["sweep"] == m) for m in ("fused", "stepwise", "graph")}
+    print(json.dumps({"sweep_fit": fits, "smallest_call_us": small, "nranks": n, "dtype": "f32", "op": "sum"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="grad7b", choices=sorted(WORKLOADS))
-    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
+    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise", "graph"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line, sweep 1 KiB .. 256 MiB per rank (8 ranks, fp32 SUM) in every "
+                         "mode and fit the alpha-beta model")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the all-reduce, time a plain 16-byte-vector device copy of BYTES bytes "
                          "(a one-rank all-gather): the practical HBM ceiling, and the reference reading for "
@@ -149,6 +228,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(args, torch, ar)
+        return
+    if args.sweep:
+        sweep(args, torch, ar, synthetic)
         return
     n, count, dtype, op, desc = WORKLOADS[args.workload]
     wl = args.workload if args.workload in synthetic.WORKLOAD_IDS else "sweep"

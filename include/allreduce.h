@@ -79,8 +79,19 @@ typedef enum { AR_SUM = 0, AR_AVG = 1, AR_MAX = 2, AR_MIN = 3, AR_PROD = 4 } ar_
  * ring's.
  * AR_MODE_RING_STEPWISE: the ring itself, one launch per ring step:
  * N-1 reduce-scatter steps then N-1 all-gather steps [P3 section 三;
- * P4 section 环形 all-reduce 与通信量]. */
-typedef enum { AR_MODE_FUSED = 0, AR_MODE_RING_STEPWISE = 1 } ar_mode_t;
+ * P4 section 环形 all-reduce 与通信量].
+ * AR_MODE_RING_GRAPH: the same ring steps, captured once into a HIP graph
+ * per call signature (collective, buffer pointers, count, dtype, op,
+ * workspace) and replayed as one graph launch afterwards, which removes the
+ * per-step launch cost that the alpha term of the alpha-beta model charges
+ * [P3 section 四; P4 section α-β 模型: graph-captured custom all-reduce].
+ * A comm keeps up to 16 graphs (least recently used evicted). The pointers
+ * in a cached graph are fixed: a later call with the same pointers and sizes
+ * replays it whatever the buffers now hold. Must not be used while `stream`
+ * is itself being captured (INVALID_ARGUMENT): capture AR_MODE_RING_STEPWISE
+ * or AR_MODE_FUSED instead -- both are capture-safe (no synchronous calls,
+ * no memsets, no allocation). Same bits as the other modes. */
+typedef enum { AR_MODE_FUSED = 0, AR_MODE_RING_STEPWISE = 1, AR_MODE_RING_GRAPH = 2 } ar_mode_t;
 
 typedef enum { AR_COLL_ALL_REDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GATHER = 2 } ar_collective_t;
 
@@ -100,9 +111,9 @@ int ar_comm_nranks(ar_comm_t comm);
 
 /* Device workspace (bytes) a call needs; 0 when none. `count` is the
  * collective's own count argument (count, recvcount or sendcount).
- * Stepwise all-reduce of fp16/bf16 keeps fp32 partial sums: 4*count bytes.
- * Stepwise reduce-scatter keeps the partials of all nranks blocks:
- * 4*nranks*recvcount bytes. Everything else: 0. Returns (size_t)-1 for
+ * The ring modes (stepwise and graph) need it: all-reduce of fp16/bf16
+ * keeps fp32 partial sums, 4*count bytes; reduce-scatter keeps the partials
+ * of all nranks blocks, 4*nranks*recvcount bytes. Everything else: 0. Returns (size_t)-1 for
  * invalid arguments or if the size overflows. */
 size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype, ar_mode_t mode);
 
@@ -121,10 +132,11 @@ ar_result_t ar_comm_set_workspace(ar_comm_t comm, void* dev_ptr, size_t bytes);
  * sendbufs[r] and recvbufs[r] each hold `count` elements of `dtype`.
  * In place is allowed (sendbufs[r] == recvbufs[r]); any other overlap
  * between any two of the 2*nranks buffers (or the workspace) is
- * INVALID_ARGUMENT. Stepwise fp16/bf16 needs a workspace of
- * ar_workspace_bytes(...) bytes, else INVALID_ARGUMENT. Pointers need not
- * be aligned; 16-byte alignment with q a multiple of 16/sizeof(dtype)
- * selects the vector kernels. */
+ * INVALID_ARGUMENT. Ring-mode fp16/bf16 needs a workspace of
+ * ar_workspace_bytes(...) bytes, else INVALID_ARGUMENT. Pointers must be
+ * aligned to the element size (else INVALID_ARGUMENT); 16-byte alignment
+ * with q a multiple of 16/sizeof(dtype) selects the vector kernels, other
+ * layouts take element-wise kernels with the same results. */
 ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
                           ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
 
@@ -133,7 +145,7 @@ ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* co
  * block c of the reduction, block c being folded in the same ring order as
  * in ar_all_reduce, so reduce-scatter followed by all-gather equals
  * all-reduce bit for bit. In place: recvbufs[r] == sendbufs[r] +
- * r*recvcount elements. Stepwise mode needs a workspace of
+ * r*recvcount elements. The ring modes need a workspace of
  * ar_workspace_bytes(...) bytes. Errors as ar_all_reduce. */
 ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
                               size_t recvcount, ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
@@ -149,8 +161,8 @@ ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[], void* co
 /* Per-step timing of stepwise calls (the alpha-beta model's per-step cost,
  * [P3 section 四; P4 section α-β 模型]). When enabled, each stepwise call
  * records a HIP event before its first step and after every step; fused
- * calls record one interval. Recording adds a little per-step overhead and
- * is not meant for graph capture. */
+ * and graph-mode calls record one interval. Recording adds a little
+ * per-step overhead and is not meant for the caller's own graph capture. */
 ar_result_t ar_comm_set_step_timing(ar_comm_t comm, int enable);
 
 /* Step durations (ms) of the last timed call on this comm: waits for that

@@ -21,6 +21,13 @@ LIB_PATH = os.path.join(_PKG, "liballreduce.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m ring_all_reduce_ar_amd.build` first")
 
+# One process must hold one HIP runtime. torch ships its own libamdhip64 /
+# libhsa-runtime64; importing torch first loads them, and liballreduce.so's
+# dependency on libamdhip64.so.7 then binds to that same runtime instead of
+# loading a second one from /opt/rocm (two HSA runtimes in one process leave
+# the second without a device).
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 MAX_RANKS = 64
@@ -32,13 +39,13 @@ AR_FLOAT32, AR_FLOAT16, AR_BFLOAT16, AR_INT32 = range(4)
 # ar_op_t
 AR_SUM, AR_AVG, AR_MAX, AR_MIN, AR_PROD = range(5)
 # ar_mode_t
-AR_MODE_FUSED, AR_MODE_RING_STEPWISE = range(2)
+AR_MODE_FUSED, AR_MODE_RING_STEPWISE, AR_MODE_RING_GRAPH = range(3)
 # ar_collective_t
 AR_COLL_ALL_REDUCE, AR_COLL_REDUCE_SCATTER, AR_COLL_ALL_GATHER = range(3)
 
 DTYPE_NAMES = {"f32": AR_FLOAT32, "f16": AR_FLOAT16, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 OP_NAMES = {"sum": AR_SUM, "avg": AR_AVG, "max": AR_MAX, "min": AR_MIN, "prod": AR_PROD}
-MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE}
+MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph": AR_MODE_RING_GRAPH}
 
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",

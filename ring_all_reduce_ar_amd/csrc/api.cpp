@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <string>
 #include <vector>
@@ -29,6 +30,16 @@ struct ar_comm {
     bool step_timing = false;
     std::vector<hipEvent_t> events;  // step boundaries of the last timed call
     int last_steps = -1;
+    // AR_MODE_RING_GRAPH: instantiated graphs keyed by call signature.
+    struct GraphEntry {
+        std::vector<uintptr_t> key;
+        hipGraphExec_t exec;
+        uint64_t last_use;
+    };
+    static constexpr size_t kMaxGraphs = 16;
+    std::vector<GraphEntry> graphs;
+    uint64_t use_clock = 0;
+    hipStream_t capture_stream = nullptr;
 };
 
 namespace {
@@ -64,7 +75,7 @@ size_t elem_size(ar_dtype_t d)
 
 bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
 bool valid_op(int o) { return o >= AR_SUM && o <= AR_PROD; }
-bool valid_mode(int m) { return m == AR_MODE_FUSED || m == AR_MODE_RING_STEPWISE; }
+bool valid_mode(int m) { return m == AR_MODE_FUSED || m == AR_MODE_RING_STEPWISE || m == AR_MODE_RING_GRAPH; }
 
 const char* dtype_name(ar_dtype_t d)
 {
@@ -227,31 +238,6 @@ bool all_aligned16(int n, const void* const send[], void* const recv[])
     return true;
 }
 
-// Local copies send[r] -> recv[r] + r*dst_stride for ranks whose buffers differ.
-ar_result_t local_copies(ar_comm* comm, int n, const void* const send[], void* const recv[], size_t bytes,
-                         size_t dst_stride, hipStream_t stream)
-{
-    ar::CopyArgs a{};
-    int m = 0;
-    bool vec = (bytes % 16 == 0) && (dst_stride % 16 == 0);
-    for (int r = 0; r < n; ++r) {
-        const char* dst = static_cast<const char*>(recv[r]) + static_cast<size_t>(r) * dst_stride;
-        if (dst == send[r]) continue;
-        // Pack only the ranks that need a copy; rank index m keeps dst offset r*dst_stride
-        // by pre-offsetting the destination pointer.
-        a.send[m] = send[r];
-        a.recv[m] = const_cast<char*>(dst);
-        vec = vec && aligned16(send[r]) && aligned16(dst);
-        ++m;
-    }
-    if (m == 0) return AR_SUCCESS;
-    a.n = m;
-    a.total = bytes;
-    a.dst_stride = 0;
-    hipError_t e = ar::launch_local_copy(a, vec, grid_for(comm, vec ? ceil_div(bytes, 16) : ceil_div(bytes, 2), m), stream);
-    return e == hipSuccess ? AR_SUCCESS : hip_fail(e, "local copy launch");
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -286,6 +272,8 @@ AR_EXPORT ar_result_t ar_comm_destroy(ar_comm_t comm)
 {
     if (!comm) return AR_SUCCESS;
     for (hipEvent_t e : comm->events) (void)hipEventDestroy(e);
+    for (auto& g : comm->graphs) (void)hipGraphExecDestroy(g.exec);
+    if (comm->capture_stream) (void)hipStreamDestroy(comm->capture_stream);
     delete comm;
     return AR_SUCCESS;
 }
@@ -295,7 +283,7 @@ AR_EXPORT int ar_comm_nranks(ar_comm_t comm) { return comm ? comm->nranks : -1; 
 AR_EXPORT size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype, ar_mode_t mode)
 {
     if (nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype(dtype) || !valid_mode(mode)) return static_cast<size_t>(-1);
-    if (mode != AR_MODE_RING_STEPWISE || nranks == 1) return 0;
+    if ((mode != AR_MODE_RING_STEPWISE && mode != AR_MODE_RING_GRAPH) || nranks == 1) return 0;
     size_t out = 0;
     if (coll == AR_COLL_ALL_REDUCE) {
         if (dtype != AR_FLOAT16 && dtype != AR_BFLOAT16) return 0;
@@ -354,6 +342,96 @@ AR_EXPORT ar_result_t ar_last_step_times_ms(ar_comm_t comm, float* out, int cap,
 // ---------------------------------------------------------------------------
 // collectives
 // ---------------------------------------------------------------------------
+namespace {
+
+// Enqueues one call's launches on a stream; `t` (may be null) records step events.
+using Enqueue = std::function<hipError_t(hipStream_t, StepTimer*)>;
+
+hipError_t tick(StepTimer* t) { return t ? t->step() : hipSuccess; }
+
+// Eager: enqueue the launches directly on the caller's stream.
+ar_result_t run_eager(ar_comm* comm, hipStream_t stream, int nsteps, const Enqueue& fn)
+{
+    StepTimer timer(comm, stream);
+    hipError_t e = timer.begin(nsteps);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = fn(stream, comm->step_timing ? &timer : nullptr);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    timer.end();
+    return AR_SUCCESS;
+}
+
+// Graph mode: the call's launches are captured once into a hipGraph per key
+// (collective, buffers, sizes, dtype, op, workspace) and the instantiated
+// graph is replayed with one launch on later calls.
+ar_result_t run_graph(ar_comm* comm, std::vector<uintptr_t>&& key, hipStream_t stream, const Enqueue& fn)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(AR_ERR_INVALID_ARGUMENT,
+                    "AR_MODE_RING_GRAPH cannot be used while the stream is being captured; use AR_MODE_RING_STEPWISE "
+                    "inside a capture");
+    ar_comm::GraphEntry* hit = nullptr;
+    for (auto& g : comm->graphs)
+        if (g.key == key) hit = &g;
+    if (!hit) {
+        if (!comm->capture_stream) {
+            e = hipStreamCreateWithFlags(&comm->capture_stream, hipStreamNonBlocking);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+        }
+        e = hipStreamBeginCapture(comm->capture_stream, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+        const hipError_t le = fn(comm->capture_stream, nullptr);
+        hipGraph_t graph = nullptr;
+        e = hipStreamEndCapture(comm->capture_stream, &graph);
+        if (le != hipSuccess || e != hipSuccess) {
+            if (graph) (void)hipGraphDestroy(graph);
+            return hip_fail(le != hipSuccess ? le : e, "graph capture");
+        }
+        hipGraphExec_t exec = nullptr;
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+        if (comm->graphs.size() >= ar_comm::kMaxGraphs) {
+            auto oldest = std::min_element(comm->graphs.begin(), comm->graphs.end(),
+                                           [](const auto& a, const auto& b) { return a.last_use < b.last_use; });
+            (void)hipGraphExecDestroy(oldest->exec);
+            comm->graphs.erase(oldest);
+        }
+        comm->graphs.push_back({std::move(key), exec, 0});
+        hit = &comm->graphs.back();
+    }
+    hit->last_use = ++comm->use_clock;
+    StepTimer timer(comm, stream);
+    e = timer.begin(1);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = hipGraphLaunch(hit->exec, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    e = timer.step();
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    timer.end();
+    return AR_SUCCESS;
+}
+
+std::vector<uintptr_t> graph_key(int coll, int n, const void* const send[], void* const recv[], size_t count, int dtype,
+                                 int op, const void* ws)
+{
+    std::vector<uintptr_t> k{static_cast<uintptr_t>(coll), static_cast<uintptr_t>(n), count,
+                             static_cast<uintptr_t>(dtype), static_cast<uintptr_t>(op),
+                             reinterpret_cast<uintptr_t>(ws)};
+    for (int r = 0; r < n; ++r) {
+        k.push_back(reinterpret_cast<uintptr_t>(send[r]));
+        k.push_back(reinterpret_cast<uintptr_t>(recv[r]));
+    }
+    return k;
+}
+
+bool ring_mode(ar_mode_t mode) { return mode == AR_MODE_RING_STEPWISE || mode == AR_MODE_RING_GRAPH; }
+
+}  // namespace
+
 AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
                                     ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
 {
@@ -365,7 +443,7 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     size_t bytes = 0;
     if (!mul_ok(count, e, &bytes)) return fail(AR_ERR_INVALID_ARGUMENT, "count %zu overflows", count);
     if (count == 0) return AR_SUCCESS;
-    const bool stepwise = mode == AR_MODE_RING_STEPWISE && n > 1;
+    const bool stepwise = ring_mode(mode) && n > 1;
     const size_t ws_need = stepwise ? ar_workspace_bytes(AR_COLL_ALL_REDUCE, n, count, dtype, mode) : 0;
     if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
     rc = need_workspace(comm, ws_need);
@@ -380,13 +458,9 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     DeviceGuard g(comm->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
     if (comm->debug)
-        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%s q=%llu vec=%d\n", n, count,
-                     dtype_name(dtype), static_cast<int>(op), stepwise ? "stepwise" : "fused",
+        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%d q=%llu vec=%d\n", n, count,
+                     dtype_name(dtype), static_cast<int>(op), static_cast<int>(mode),
                      static_cast<unsigned long long>(q), vec ? 1 : 0);
-
-    StepTimer timer(comm, stream);
-    hipError_t err = timer.begin(stepwise ? 2 * (n - 1) : 1);
-    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
 
     if (!stepwise) {
         ar::ReduceArgs a{};
@@ -395,11 +469,10 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         a.q = q;
         a.n = n;
         const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
-        err = ar::launch_fused_reduce(a, dtype, op, false, vec, gx, stream);
-        if (err != hipSuccess) return hip_fail(err, "fused all-reduce launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-        timer.end();
-        return AR_SUCCESS;
+        return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, gx, s);
+            return err != hipSuccess ? err : tick(t);
+        });
     }
 
     // Reduce-scatter: n-1 steps. fp32/int32 partials travel in the recv
@@ -413,14 +486,6 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     sa.n = n;
     sa.scatter = 0;
     const int gx_rs = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
-    for (int s = 0; s < n - 1; ++s) {
-        sa.s = s;
-        sa.first = s == 0;
-        sa.last = s == n - 2;
-        err = ar::launch_rs_step(sa, dtype, op, vec, gx_rs, stream);
-        if (err != hipSuccess) return hip_fail(err, "reduce-scatter step launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    }
     // All-gather: n-1 copy steps; step s moves chunk (r - s) mod n from rank r-1 to rank r.
     ar::CopyArgs ca{};
     for (int r = 0; r < n; ++r) ca.recv[r] = recvbufs[r];
@@ -430,14 +495,26 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     ca.shift = 0;
     const bool cvec = all_aligned16(n, sendbufs, recvbufs) && (ca.qb % 16 == 0);
     const int gx_ag = grid_for(comm, cvec ? ceil_div(ca.qb, 16) : ceil_div(ca.qb, 2), n);
-    for (int s = 0; s < n - 1; ++s) {
-        ca.s = s;
-        err = ar::launch_copy_step(ca, cvec, gx_ag, stream);
-        if (err != hipSuccess) return hip_fail(err, "all-gather step launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    }
-    timer.end();
-    return AR_SUCCESS;
+    Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
+        for (int st = 0; st < n - 1; ++st) {
+            sa.s = st;
+            sa.first = st == 0;
+            sa.last = st == n - 2;
+            hipError_t err = ar::launch_rs_step(sa, dtype, op, vec, gx_rs, s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        for (int st = 0; st < n - 1; ++st) {
+            ca.s = st;
+            hipError_t err = ar::launch_copy_step(ca, cvec, gx_ag, s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    };
+    if (mode == AR_MODE_RING_GRAPH)
+        return run_graph(comm, graph_key(AR_COLL_ALL_REDUCE, n, sendbufs, recvbufs, count, dtype, op, sa.ws), stream, fn);
+    return run_eager(comm, stream, 2 * (n - 1), fn);
 }
 
 AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
@@ -453,7 +530,7 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
     if (!mul_ok(recvcount, e, &rbytes) || !mul_ok(recvcount, static_cast<size_t>(n), &total) || !mul_ok(total, e, &sbytes))
         return fail(AR_ERR_INVALID_ARGUMENT, "recvcount %zu overflows", recvcount);
     if (recvcount == 0) return AR_SUCCESS;
-    const bool stepwise = mode == AR_MODE_RING_STEPWISE && n > 1;
+    const bool stepwise = ring_mode(mode) && n > 1;
     const size_t ws_need = stepwise ? ar_workspace_bytes(AR_COLL_REDUCE_SCATTER, n, recvcount, dtype, mode) : 0;
     if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
     rc = need_workspace(comm, ws_need);
@@ -467,11 +544,9 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
     DeviceGuard g(comm->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
     if (comm->debug)
-        std::fprintf(stderr, "[allreduce] reduce_scatter n=%d recvcount=%zu dtype=%s op=%d mode=%s vec=%d\n", n,
-                     recvcount, dtype_name(dtype), static_cast<int>(op), stepwise ? "stepwise" : "fused", vec ? 1 : 0);
-    StepTimer timer(comm, stream);
-    hipError_t err = timer.begin(stepwise ? n - 1 : 1);
-    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+        std::fprintf(stderr, "[allreduce] reduce_scatter n=%d recvcount=%zu dtype=%s op=%d mode=%d vec=%d\n", n,
+                     recvcount, dtype_name(dtype), static_cast<int>(op), static_cast<int>(mode), vec ? 1 : 0);
+    const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
 
     if (!stepwise) {
         ar::ReduceArgs a{};
@@ -479,11 +554,10 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.count = total;
         a.q = q;
         a.n = n;
-        err = ar::launch_fused_reduce(a, dtype, op, true, vec, grid_for(comm, vec ? ceil_div(q, epv) : q, n), stream);
-        if (err != hipSuccess) return hip_fail(err, "fused reduce-scatter launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-        timer.end();
-        return AR_SUCCESS;
+        return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, gx, s);
+            return err != hipSuccess ? err : tick(t);
+        });
     }
     // The ring's reduce-scatter phase with partials in the workspace; the
     // last step writes finished chunk c to recvbufs[c].
@@ -494,17 +568,21 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
     sa.q = q;
     sa.n = n;
     sa.scatter = 1;
-    const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n);
-    for (int s = 0; s < n - 1; ++s) {
-        sa.s = s;
-        sa.first = s == 0;
-        sa.last = s == n - 2;
-        err = ar::launch_rs_step(sa, dtype, op, vec, gx, stream);
-        if (err != hipSuccess) return hip_fail(err, "reduce-scatter step launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    }
-    timer.end();
-    return AR_SUCCESS;
+    Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
+        for (int st = 0; st < n - 1; ++st) {
+            sa.s = st;
+            sa.first = st == 0;
+            sa.last = st == n - 2;
+            hipError_t err = ar::launch_rs_step(sa, dtype, op, vec, gx, s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    };
+    if (mode == AR_MODE_RING_GRAPH)
+        return run_graph(comm, graph_key(AR_COLL_REDUCE_SCATTER, n, sendbufs, recvbufs, recvcount, dtype, op, sa.ws),
+                         stream, fn);
+    return run_eager(comm, stream, n - 1, fn);
 }
 
 AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
@@ -520,48 +598,63 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
     if (sendcount == 0) return AR_SUCCESS;
     rc = check_buffers(n, sendbufs, recvbufs, blk, rbytes, AR_COLL_ALL_GATHER, e, nullptr, 0);
     if (rc != AR_SUCCESS) return rc;
-    const bool stepwise = mode == AR_MODE_RING_STEPWISE && n > 1;
+    const bool stepwise = ring_mode(mode) && n > 1;
     const bool vec = all_aligned16(n, sendbufs, recvbufs) && blk % 16 == 0;
     DeviceGuard g(comm->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
     if (comm->debug)
-        std::fprintf(stderr, "[allreduce] all_gather n=%d sendcount=%zu dtype=%s mode=%s vec=%d\n", n, sendcount,
-                     dtype_name(dtype), stepwise ? "stepwise" : "fused", vec ? 1 : 0);
-    StepTimer timer(comm, stream);
-    hipError_t err = timer.begin(stepwise ? n : 1);
-    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+        std::fprintf(stderr, "[allreduce] all_gather n=%d sendcount=%zu dtype=%s mode=%d vec=%d\n", n, sendcount,
+                     dtype_name(dtype), static_cast<int>(mode), vec ? 1 : 0);
+    const int gx = grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n);
 
     if (!stepwise) {
         ar::CopyArgs a{};
         fill_ptrs(a, n, sendbufs, recvbufs);
         a.total = blk;
         a.n = n;
-        err = ar::launch_fused_gather(a, vec, grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n), stream);
-        if (err != hipSuccess) return hip_fail(err, "fused all-gather launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-        timer.end();
-        return AR_SUCCESS;
+        return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
+            hipError_t err = ar::launch_fused_gather(a, vec, gx, s);
+            return err != hipSuccess ? err : tick(t);
+        });
     }
     // Each rank first places its own block (unless in place), then n-1 ring
     // steps: at step s rank r receives block (r - s - 1) mod n from rank r-1.
-    rc = local_copies(comm, n, sendbufs, recvbufs, blk, blk, stream);
-    if (rc != AR_SUCCESS) return rc;
-    if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
+    ar::CopyArgs la{};
+    int m = 0;
+    bool lvec = vec;
+    for (int r = 0; r < n; ++r) {
+        const char* dst = static_cast<const char*>(recvbufs[r]) + static_cast<size_t>(r) * blk;
+        if (dst == sendbufs[r]) continue;
+        la.send[m] = sendbufs[r];
+        la.recv[m] = const_cast<char*>(dst);
+        ++m;
+    }
+    la.n = m;
+    la.total = blk;
+    la.dst_stride = 0;
+    const int gx_local = grid_for(comm, lvec ? ceil_div(blk, 16) : ceil_div(blk, 2), std::max(m, 1));
     ar::CopyArgs ca{};
     for (int r = 0; r < n; ++r) ca.recv[r] = recvbufs[r];
     ca.total = rbytes;
     ca.qb = blk;
     ca.n = n;
     ca.shift = 1;
-    const int gx = grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n);
-    for (int s = 0; s < n - 1; ++s) {
-        ca.s = s;
-        err = ar::launch_copy_step(ca, vec, gx, stream);
-        if (err != hipSuccess) return hip_fail(err, "all-gather step launch");
-        if ((err = timer.step()) != hipSuccess) return hip_fail(err, "hipEventRecord");
-    }
-    timer.end();
-    return AR_SUCCESS;
+    Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
+        hipError_t err = m > 0 ? ar::launch_local_copy(la, lvec, gx_local, s) : hipSuccess;
+        if (err == hipSuccess) err = tick(t);
+        if (err != hipSuccess) return err;
+        for (int st = 0; st < n - 1; ++st) {
+            ca.s = st;
+            err = ar::launch_copy_step(ca, vec, gx, s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    };
+    if (mode == AR_MODE_RING_GRAPH)
+        return run_graph(comm, graph_key(AR_COLL_ALL_GATHER, n, sendbufs, recvbufs, sendcount, dtype, 0, nullptr),
+                         stream, fn);
+    return run_eager(comm, stream, n, fn);
 }
 
 AR_EXPORT const char* ar_result_string(ar_result_t result)

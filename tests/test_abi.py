@@ -81,3 +81,17 @@ def test_bench_refuses_more_than_one_gpu():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"], capture_output=True,
                        text=True, timeout=120)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_one_hip_runtime_in_the_process():
+    """Importing the binding maps exactly one libamdhip64 and one HSA runtime
+    (torch's), even when nothing imported torch before it."""
+    import subprocess
+    import sys
+    code = ("import ring_all_reduce_ar_amd\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = {l.split()[-1] for l in maps if 'amdhip64' in l or 'hsa-runtime64' in l}\n"
+            "print(len([x for x in libs if 'amdhip64' in x]), len([x for x in libs if 'hsa-runtime64' in x]))\n")
+    p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.split() == ["1", "1"], p.stdout
