@@ -93,7 +93,12 @@ typedef enum { AR_SUM = 0, AR_AVG = 1, AR_MAX = 2, AR_MIN = 3, AR_PROD = 4 } ar_
  * no memsets, no allocation). Same bits as the other modes. */
 typedef enum { AR_MODE_FUSED = 0, AR_MODE_RING_STEPWISE = 1, AR_MODE_RING_GRAPH = 2 } ar_mode_t;
 
-typedef enum { AR_COLL_ALL_REDUCE = 0, AR_COLL_REDUCE_SCATTER = 1, AR_COLL_ALL_GATHER = 2 } ar_collective_t;
+typedef enum {
+    AR_COLL_ALL_REDUCE = 0,
+    AR_COLL_REDUCE_SCATTER = 1,
+    AR_COLL_ALL_GATHER = 2,
+    AR_COLL_ALL_TO_ALL = 3
+} ar_collective_t;
 
 /* Create a communicator for `nranks` (1..AR_MAX_RANKS) virtual ranks on HIP
  * device `hip_device`. On success *comm owns host state and a few HIP
@@ -156,6 +161,17 @@ ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbufs[], void
  * sendbufs[r] == recvbufs[r] + r*sendcount elements. Errors as
  * ar_all_reduce (no workspace is needed). */
 ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t sendcount,
+                          ar_dtype_t dtype, ar_mode_t mode, hipStream_t stream);
+
+/* All-to-all, the "transpose" primitive [P4 section 五个原语 (all_to_all_single:
+ * rank r's p-th block goes to rank p); P3 section 六]: sendbufs[r] holds
+ * nranks blocks of blockcount elements; block r of recvbufs[p] receives
+ * block p of sendbufs[r], for every r and p. Each rank sends (n-1)/n of its
+ * data. AR_MODE_FUSED moves every block in one launch; the ring modes take n
+ * steps, step s moving block (r + s) mod n of every rank r (step 0 is each
+ * rank's own block). No workspace. Send and recv buffers must not overlap at
+ * all (there is no in-place form); errors otherwise as ar_all_reduce. */
+ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t blockcount,
                           ar_dtype_t dtype, ar_mode_t mode, hipStream_t stream);
 
 /* Per-step timing of stepwise calls (the alpha-beta model's per-step cost,

@@ -63,6 +63,7 @@ class Oracle:
         lib.orc_reduce_scatter.argtypes = [i32, u64, i32, i32, pp, pp, pu64]
         lib.orc_all_gather.argtypes = [i32, u64, i32, pp, pp, pu64]
         lib.orc_chunk_bounds.argtypes = [i32, u64, i32, pu64, pu64]
+        lib.orc_all_to_all.argtypes = [i32, u64, i32, pp, pp, pu64]
         for name in ("orc_f32_to_f16", "orc_f16_to_f32", "orc_f32_to_bf16", "orc_bf16_to_f32"):
             getattr(lib, name).argtypes = [vp, vp, u64]
             getattr(lib, name).restype = None
@@ -123,6 +124,18 @@ class Oracle:
         outs = [np.empty(n * sc, dtype=NP_DTYPE[dtype]) for _ in range(n)]
         sent = (ctypes.c_uint64 * n)()
         _rc(self.lib.orc_all_gather(n, sc, DTYPES[dtype], _ptrs(inputs), _ptrs(outs), sent), "all_gather")
+        return (outs, [int(s) for s in sent]) if with_sent else outs
+
+    def all_to_all(self, inputs, dtype: str, with_sent: bool = False):
+        """All-to-all: inputs[r] holds n blocks; outs[p] block r = inputs[r] block p."""
+        n = len(inputs)
+        total = inputs[0].size
+        _check_bufs(inputs, dtype, total)
+        if total % n:
+            raise ValueError("all_to_all input size must be a multiple of the rank count")
+        outs = [np.empty(total, dtype=NP_DTYPE[dtype]) for _ in range(n)]
+        sent = (ctypes.c_uint64 * n)()
+        _rc(self.lib.orc_all_to_all(n, total // n, DTYPES[dtype], _ptrs(inputs), _ptrs(outs), sent), "all_to_all")
         return (outs, [int(s) for s in sent]) if with_sent else outs
 
     def chunk_bounds(self, n: int, count: int):
@@ -202,6 +215,10 @@ def reduce_scatter(inputs, dtype, op, with_sent=False):
 
 def all_gather(inputs, dtype, with_sent=False):
     return get().all_gather(inputs, dtype, with_sent)
+
+
+def all_to_all(inputs, dtype, with_sent=False):
+    return get().all_to_all(inputs, dtype, with_sent)
 
 
 def chunk_bounds(n, count):

@@ -22,7 +22,9 @@
  *       sends chunk (rank - s) to the right and adds the received chunk into
  *       chunk (rank - s - 1); all-gather step s sends chunk (rank + 1 - s) and
  *       copies the received one into chunk (rank - s); bytes sent counted as
- *       numel * element_size per send).
+ *       numel * element_size per send); all_to_all in section 五个原语: rank
+ *       r's p-th block goes to rank p, which stores it as its r-th block; each
+ *       rank sends (n-1)/n of its data (its own block stays).
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - partition: q = ceil(count / N); chunk c = [c*q, min((c+1)*q, count)),
@@ -508,6 +510,27 @@ int orc_all_gather(int n, uint64_t sendcount, int dtype, const void* const* in, 
     }
     for (int r = 0; r < n; r++) free(msg[r]);
     free(msg);
+    return ORC_OK;
+}
+
+/*
+ * All-to-all: in[r] holds n blocks of blockcount elements; block p of rank r
+ * is sent to rank p, which stores it as block r of out[p]. Rank r's own
+ * block is a local copy and is not counted in sent[r]. in and out must not
+ * overlap.
+ */
+int orc_all_to_all(int n, uint64_t blockcount, int dtype, const void* const* in, void* const* out, uint64_t* sent)
+{
+    if (!valid(n, dtype, ORC_SUM) || !in || !out)
+        return ORC_EINVAL;
+    size_t blk = (size_t)blockcount * elem_size(dtype);
+    for (int r = 0; r < n; r++) {
+        if (sent) sent[r] = 0;
+        for (int p = 0; p < n; p++) {
+            memcpy((unsigned char*)out[p] + (size_t)r * blk, (const unsigned char*)in[r] + (size_t)p * blk, blk);
+            if (sent && p != r) sent[r] += blk;
+        }
+    }
     return ORC_OK;
 }
 

@@ -7,7 +7,7 @@ passed as torch tensors (their ``data_ptr()`` is taken) or as integer device
 addresses; streams as ``torch.cuda.Stream``, an integer ``hipStream_t`` or
 ``None`` (torch's current stream on the comm's device).
 
-The library is built in-tree by ``python -m ring_all_reduce_ar_amd.build``;
+The library is built in-tree by ``python ring_all_reduce_ar_amd/build.py``;
 importing this package without it raises ImportError: there is no fallback.
 """
 from __future__ import annotations
@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liballreduce.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m ring_all_reduce_ar_amd.build` first")
+    raise ImportError(f"{LIB_PATH} is not built; run `python ring_all_reduce_ar_amd/build.py` first")
 
 # One process must hold one HIP runtime. torch ships its own libamdhip64 /
 # libhsa-runtime64; importing torch first loads them, and liballreduce.so's
@@ -41,7 +41,7 @@ AR_SUM, AR_AVG, AR_MAX, AR_MIN, AR_PROD = range(5)
 # ar_mode_t
 AR_MODE_FUSED, AR_MODE_RING_STEPWISE, AR_MODE_RING_GRAPH = range(3)
 # ar_collective_t
-AR_COLL_ALL_REDUCE, AR_COLL_REDUCE_SCATTER, AR_COLL_ALL_GATHER = range(3)
+AR_COLL_ALL_REDUCE, AR_COLL_REDUCE_SCATTER, AR_COLL_ALL_GATHER, AR_COLL_ALL_TO_ALL = range(4)
 
 DTYPE_NAMES = {"f32": AR_FLOAT32, "f16": AR_FLOAT16, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 OP_NAMES = {"sum": AR_SUM, "avg": AR_AVG, "max": AR_MAX, "min": AR_MIN, "prod": AR_PROD}
@@ -49,7 +49,8 @@ MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph"
 
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",
-    "ar_all_reduce", "ar_reduce_scatter", "ar_all_gather", "ar_comm_set_step_timing", "ar_last_step_times_ms",
+    "ar_all_reduce", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_comm_set_step_timing",
+    "ar_last_step_times_ms",
     "ar_result_string", "ar_last_error",
 )
 
@@ -66,6 +67,7 @@ _lib.ar_comm_set_workspace.argtypes = [_vp, _vp, _c_size]
 _lib.ar_all_reduce.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _c_int, _vp]
 _lib.ar_reduce_scatter.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _c_int, _vp]
 _lib.ar_all_gather.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _vp]
+_lib.ar_all_to_all.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _vp]
 _lib.ar_comm_set_step_timing.argtypes = [_vp, _c_int]
 _lib.ar_last_step_times_ms.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]
 _lib.ar_result_string.argtypes = [_c_int]
@@ -73,7 +75,7 @@ _lib.ar_result_string.restype = ctypes.c_char_p
 _lib.ar_last_error.argtypes = []
 _lib.ar_last_error.restype = ctypes.c_char_p
 for _name in ("ar_comm_create", "ar_comm_destroy", "ar_comm_set_workspace", "ar_all_reduce", "ar_reduce_scatter",
-              "ar_all_gather", "ar_comm_set_step_timing", "ar_last_step_times_ms"):
+              "ar_all_gather", "ar_all_to_all", "ar_comm_set_step_timing", "ar_last_step_times_ms"):
     getattr(_lib, _name).restype = _c_int
 
 
@@ -215,6 +217,12 @@ def ar_all_gather(comm, sendbufs, recvbufs, sendcount: int, dtype, mode="fused",
     _check(_lib.ar_all_gather(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), sendcount,
                               _enum(dtype, DTYPE_NAMES, "dtype"), _enum(mode, MODE_NAMES, "mode"),
                               _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_gather")
+
+
+def ar_all_to_all(comm, sendbufs, recvbufs, blockcount: int, dtype, mode="fused", stream=None):
+    _check(_lib.ar_all_to_all(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), blockcount,
+                              _enum(dtype, DTYPE_NAMES, "dtype"), _enum(mode, MODE_NAMES, "mode"),
+                              _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_to_all")
 
 
 def ar_comm_set_step_timing(comm, enable: bool):

@@ -1,6 +1,9 @@
 """Build liballreduce.so in-tree with hipcc for gfx950.
 
-    python -m ring_all_reduce_ar_amd.build
+    python ring_all_reduce_ar_amd/build.py
+
+(Run it as a file, not with -m: importing the package loads the library,
+which may be missing or stale before the build.)
 
 Flags: -O3; no FMA contraction (-ffp-contract=off) so sums and products are
 rounded exactly as written; packed-fp32 instructions disabled

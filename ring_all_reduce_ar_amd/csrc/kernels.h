@@ -54,6 +54,19 @@ struct CopyArgs {
     int shift;
 };
 
+// All-to-all block copies: row y copies block p of send[r] to block r of
+// recv[p], `blk` bytes. step < 0: all n*n (r, p) pairs, row y = r*n + p;
+// step s >= 0: the n pairs (r, (r + s) mod n), row y = r.
+struct A2AArgs {
+    const void* send[AR_MAX_RANKS];
+    void* recv[AR_MAX_RANKS];
+    uint64_t blk;
+    int n;
+    int step;
+};
+
+hipError_t launch_all_to_all(const A2AArgs& a, bool vec, int grid_x, hipStream_t stream);
+
 // Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
 // has checked alignment and q % (16/elem) == 0).
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec,

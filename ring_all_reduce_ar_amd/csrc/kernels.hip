@@ -519,6 +519,35 @@ __global__ __launch_bounds__(kBlock) void local_copy(const CopyArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// all-to-all [handbook "集合通信原语", section 五个原语]: rank r's block p
+// becomes rank p's block r
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void a2a_copy(const A2AArgs a)
+{
+    const int y = blockIdx.y;
+    int r, p;
+    if (a.step < 0) {
+        r = y / a.n;
+        p = y - r * a.n;
+    } else {
+        r = y;
+        p = wrap_rank(y + a.step, a.n);
+    }
+    const char* src = static_cast<const char*>(a.send[r]) + static_cast<uint64_t>(p) * a.blk;
+    char* dst = static_cast<char*>(a.recv[p]) + static_cast<uint64_t>(r) * a.blk;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if constexpr (VEC) {
+        const uint64_t nv = a.blk / 16;
+        for (uint64_t v = t0; v < nv; v += stride) st16_nt(dst, v, ld16_nt(src, v));
+    } else {
+        for (uint64_t b = 2 * t0; b < a.blk; b += 2 * stride)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 template <class F, int OP, bool SC>
@@ -623,6 +652,14 @@ hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t
     const dim3 grid(grid_x, a.n);
     if (vec) hipLaunchKernelGGL((copy_step<true>), grid, dim3(kBlock), 0, stream, a);
     else hipLaunchKernelGGL((copy_step<false>), grid, dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_all_to_all(const A2AArgs& a, bool vec, int grid_x, hipStream_t stream)
+{
+    const dim3 grid(grid_x, a.step < 0 ? a.n * a.n : a.n);
+    if (vec) hipLaunchKernelGGL((a2a_copy<true>), grid, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((a2a_copy<false>), grid, dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 

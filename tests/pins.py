@@ -416,11 +416,40 @@ def pin_elements_match(o):
                 assert same_bits(got, full[idx]), (n, dt, op)
 
 
+def pin_all_to_all(o):
+    """All-to-all: the handbook's printed output (rank p gets [p, 10+p, 20+p,
+    30+p]), numpy's transpose of the (rank, block) grid, applying it twice
+    gives the input back, and each rank sends (n-1)/n of its data
+    (handbook "集合通信原语", sections 五个原语 and 环形 all-reduce 与通信量)."""
+    g = goldens.load("collectives_4rank_example.txt")
+    n = int(g["nranks"])
+    for dt in DTYPES:
+        xs = [as_dtype(numbers(g[f"input.{r}"]), dt) for r in range(n)]
+        outs, sent = o.all_to_all(xs, dt, with_sent=True)
+        for p in range(n):
+            assert to_f64(outs[p], dt).tolist() == numbers(g[f"all_to_all.{p}"]), (dt, p, outs[p])
+        assert sent == [(n - 1) * ELEM[dt]] * n, sent
+    rng = np.random.default_rng(43)
+    for n in (1, 2, 3, 5, 8):
+        for dt in DTYPES:
+            bc = 7
+            xs = random_inputs(rng, n, n * bc, dt, "sum")
+            outs, sent = o.all_to_all(xs, dt, with_sent=True)
+            grid = np.stack(xs).reshape(n, n, bc)
+            exp = np.ascontiguousarray(grid.transpose(1, 0, 2)).reshape(n, n * bc)
+            for p in range(n):
+                assert same_bits(outs[p], exp[p]), (n, dt, p)
+            back = o.all_to_all(outs, dt)
+            for r in range(n):
+                assert same_bits(back[r], xs[r]), (n, dt, r)
+            assert sent == [(n - 1) * bc * ELEM[dt]] * n
+
+
 ALL_PINS = [
     pin_worked_example, pin_bytes_sent_page, pin_bytes_closed_form, pin_partition_torch_chunk,
     pin_ring_order, pin_fp32_accumulate, pin_forms_agree, pin_int_brute_force, pin_fp_maxmin,
     pin_sum_error_bound, pin_avg_pow2, pin_prod_bound, pin_f16_conversions, pin_bf16_conversions,
-    pin_rs_ag_equals_ar, pin_all_gather_concat, pin_elements_match,
+    pin_rs_ag_equals_ar, pin_all_gather_concat, pin_elements_match, pin_all_to_all,
 ]
 
 

@@ -122,3 +122,9 @@ def test_comm_create_limits():
         ar.Comm(ar.MAX_RANKS + 1, 0)
     with pytest.raises(ar.ArError):
         ar.Comm(4, 1 << 20)
+
+
+def test_all_to_all_rejects_in_place(comm):
+    s = bufs(count=4 * 16)
+    expect_invalid(ar.ar_all_to_all, comm, [b.ptr() for b in s], [b.ptr() for b in s], 16, "f32", "fused", None)
+    assert untouched(s)

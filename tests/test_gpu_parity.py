@@ -249,3 +249,40 @@ def test_step_timing(comm_for):
         ar.ar_comm_set_step_timing(comm, False)
     with pytest.raises(ar.ArError):
         ar.ar_last_step_times_ms(comm)
+
+
+def _all_to_all(comm, xs, dtype, mode):
+    n = len(xs)
+    total = xs[0].numel()
+    send = [gu.RankBuf(total, dtype) for _ in range(n)]
+    for b, x in zip(send, xs):
+        b.view.copy_(x)
+    recv = [gu.RankBuf(total, dtype) for _ in range(n)]
+    ar.ar_all_to_all(comm, [b.ptr() for b in send], [b.ptr() for b in recv], total // n, dtype, mode)
+    torch.cuda.synchronize()
+    for b in send + recv:
+        assert b.guards_ok()
+    return [gu.host(b.view) for b in recv]
+
+
+def test_all_to_all_worked_example(comm_for):
+    """Rank p receives [p, 10+p, 20+p, 30+p] (handbook, section 五个原语)."""
+    g = goldens.load("collectives_4rank_example.txt")
+    for mode in ("fused", "stepwise", "graph"):
+        xs = [torch.tensor(goldens.numbers(g[f"input.{r}"]), dtype=torch.float32, device="cuda") for r in range(4)]
+        got = _all_to_all(comm_for(4), xs, "f32", mode)
+        for p in range(4):
+            assert got[p].astype(np.float64).tolist() == goldens.numbers(g[f"all_to_all.{p}"]), (mode, p, got[p])
+
+
+@pytest.mark.parametrize("mode", ("fused", "stepwise", "graph"))
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n", (1, 2, 3, 4, 8, 16, 64))
+def test_all_to_all_parity(comm_for, n, dtype, mode):
+    comm = comm_for(n)
+    for bc in (1, 2048 + gu.EPV[dtype], 1000 + 3):
+        xs = gu.make_inputs(n, n * bc, dtype, "sum", seed=bc + 3 * n)
+        exp = oracle.all_to_all([gu.host(x) for x in xs], dtype)
+        got = _all_to_all(comm, xs, dtype, mode)
+        for p in range(n):
+            gu.assert_same(got[p], exp[p], dtype, f"A2A n={n} {dtype} {mode} bc={bc} rank {p}")

@@ -48,6 +48,9 @@ MUTANTS = [
     ("f16_accumulates_in_f16", "acc = combine(dtype, op, widen(dtype, in[(c + k) % n], i), acc);",
      "acc = combine(dtype, op, widen(dtype, in[(c + k) % n], i), acc);\n"
      "            if (dtype == ORC_F16) acc.f = half_to_float(float_to_half(acc.f));"),
+    ("alltoall_transposed_wrong", "memcpy((unsigned char*)out[p] + (size_t)r * blk, (const unsigned char*)in[r] + (size_t)p * blk, blk);",
+     "memcpy((unsigned char*)out[p] + (size_t)p * blk, (const unsigned char*)in[r] + (size_t)r * blk, blk);"),
+    ("alltoall_counts_own_block", "if (sent && p != r) sent[r] += blk;", "if (sent) sent[r] += blk;"),
     ("allgather_block_order", "memmove((unsigned char*)out[r] + (size_t)r * blk, in[r], blk);",
      "memmove((unsigned char*)out[r] + (size_t)((r + 1) % n) * blk, in[r], blk);"),
 ]
