@@ -64,6 +64,7 @@ class Oracle:
         lib.orc_all_gather.argtypes = [i32, u64, i32, pp, pp, pu64]
         lib.orc_chunk_bounds.argtypes = [i32, u64, i32, pu64, pu64]
         lib.orc_all_to_all.argtypes = [i32, u64, i32, pp, pp, pu64]
+        lib.orc_tree_all_reduce.argtypes = [i32, u64, i32, i32, pp, pp, pu64]
         for name in ("orc_f32_to_f16", "orc_f16_to_f32", "orc_f32_to_bf16", "orc_bf16_to_f32"):
             getattr(lib, name).argtypes = [vp, vp, u64]
             getattr(lib, name).restype = None
@@ -124,6 +125,16 @@ class Oracle:
         outs = [np.empty(n * sc, dtype=NP_DTYPE[dtype]) for _ in range(n)]
         sent = (ctypes.c_uint64 * n)()
         _rc(self.lib.orc_all_gather(n, sc, DTYPES[dtype], _ptrs(inputs), _ptrs(outs), sent), "all_gather")
+        return (outs, [int(s) for s in sent]) if with_sent else outs
+
+    def tree_all_reduce(self, inputs, dtype: str, op: str, with_sent: bool = False):
+        """Tree-order all-reduce (pairwise levels up to rank 0, then broadcast down)."""
+        n = len(inputs)
+        count = inputs[0].size
+        _check_bufs(inputs, dtype, count)
+        outs = [np.empty(count, dtype=NP_DTYPE[dtype]) for _ in range(n)]
+        sent = (ctypes.c_uint64 * n)()
+        _rc(self.lib.orc_tree_all_reduce(n, count, DTYPES[dtype], OPS[op], _ptrs(inputs), _ptrs(outs), sent), "tree")
         return (outs, [int(s) for s in sent]) if with_sent else outs
 
     def all_to_all(self, inputs, dtype: str, with_sent: bool = False):
@@ -219,6 +230,10 @@ def all_gather(inputs, dtype, with_sent=False):
 
 def all_to_all(inputs, dtype, with_sent=False):
     return get().all_to_all(inputs, dtype, with_sent)
+
+
+def tree_all_reduce(inputs, dtype, op, with_sent=False):
+    return get().tree_all_reduce(inputs, dtype, op, with_sent)
 
 
 def chunk_bounds(n, count):

@@ -14,7 +14,10 @@
  *  [P3] geek-doc.cn, "训练梯度同步与集合通信:从参数服务器到 Ring AllReduce":
  *       section 三 (the two ring phases, the 4-GPU walk-through: chunk 0 grows
  *       as g0+g1, then +g2, then +g3; the result is the sum divided by N),
- *       section 四 (per-rank traffic 2(N-1)/N * M).
+ *       section 四 (per-rank traffic 2(N-1)/N * M), section 六 (tree
+ *       reduction: cards add in pairs, the results add in pairs again, after
+ *       log2(N) levels the root holds the result, which is then broadcast back
+ *       down the tree).
  *  [P4] anrans.github.io handbook, "集合通信原语": section 五个原语 (printed
  *       4-rank example; reduce_scatter gives rank r block r; all_gather
  *       concatenates in rank order) and section 环形 all-reduce 与通信量
@@ -510,6 +513,47 @@ int orc_all_gather(int n, uint64_t sendcount, int dtype, const void* const* in, 
     }
     for (int r = 0; r < n; r++) free(msg[r]);
     free(msg);
+    return ORC_OK;
+}
+
+/*
+ * Tree all-reduce, the literal form: level l = 0, 1, ... pairs rank r (r a
+ * multiple of 2^(l+1)) with rank r + 2^l when that rank exists; the partner
+ * sends its partial and r combines local (+) incoming. After the last level
+ * rank 0 holds the reduction; it applies AVG and rounds to the storage type,
+ * and the levels are walked back down, each parent sending the result to its
+ * child. sent[r] (may be NULL) counts storage-type bytes per send. in and out
+ * may be the same buffers.
+ */
+int orc_tree_all_reduce(int n, uint64_t count, int dtype, int op, const void* const* in, void* const* out,
+                        uint64_t* sent)
+{
+    if (!valid(n, dtype, op) || !in || !out)
+        return ORC_EINVAL;
+    size_t e = elem_size(dtype);
+    size_t bytes = (size_t)count * e;
+    if (sent) for (int r = 0; r < n; r++) sent[r] = 0;
+    if (count == 0)
+        return ORC_OK;
+    acc_t** W = widen_ranks(n, count, dtype, in);
+    if (!W) return ORC_ENOMEM;
+    int top = 1; /* 2^levels >= n */
+    while (top < n) top *= 2;
+    for (int stride = 1; stride < n; stride *= 2) {
+        for (int r = 0; r + stride < n; r += 2 * stride) {
+            int q = r + stride;
+            for (uint64_t i = 0; i < count; i++) W[r][i] = combine(dtype, op, W[r][i], W[q][i]);
+            if (sent) sent[q] += bytes;
+        }
+    }
+    for (uint64_t i = 0; i < count; i++) narrow(dtype, finalize(dtype, op, n, W[0][i]), out[0], i);
+    free_ranks(n, W);
+    for (int stride = top / 2; stride >= 1; stride /= 2) {
+        for (int r = 0; r + stride < n; r += 2 * stride) {
+            memcpy(out[r + stride], out[r], bytes);
+            if (sent) sent[r] += bytes;
+        }
+    }
     return ORC_OK;
 }
 

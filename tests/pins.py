@@ -445,11 +445,59 @@ def pin_all_to_all(o):
             assert sent == [(n - 1) * bc * ELEM[dt]] * n
 
 
+def pin_tree(o):
+    """Tree-order variant (geek-doc page, section 六): the printed integer
+    example, the hand-derived fp32 order (tree (x0+x1)+(x2+x3) against the
+    ring's chunk orders), order-free ops equal to the ring, the pairwise
+    summation bound gamma_ceil(log2 N) * sum|x| (Higham, section 4.2), the
+    closed-form tolerance 4*N*eps*sum|x| against the ring, and bytes sent:
+    every edge carries S up and S down (2(N-1)S in all), the root sends
+    ceil(log2 N)*S, odd ranks (leaves) send S."""
+    g = goldens.load("collectives_4rank_example.txt")
+    xs = [as_dtype(numbers(g[f"input.{r}"]), "f32") for r in range(4)]
+    for r, out in enumerate(o.tree_all_reduce(xs, "f32", "sum")):
+        assert out.astype(np.float64).tolist() == numbers(g[f"all_reduce.{r}"])
+    t = goldens.load("tree_order_fp32.txt")
+    xs = [as_dtype(numbers(t[f"input.{r}"]), "f32") for r in range(4)]
+    for op in ("sum", "avg"):
+        for out in o.tree_all_reduce(xs, "f32", op):
+            assert out.astype(np.float64).tolist() == numbers(t[f"tree.{op}"]), (op, out)
+    assert o.fold_all_reduce(xs, "f32", "sum")[0].astype(np.float64).tolist() == numbers(t["ring.sum"])
+    rng = np.random.default_rng(47)
+    eps = 2.0 ** -23
+    for n in (1, 2, 3, 4, 5, 7, 8, 9, 16, 64):
+        for dt in DTYPES:
+            for op in OPS:
+                xs = random_inputs(rng, n, 33, dt, op)
+                tree, sent = o.tree_all_reduce(xs, dt, op, with_sent=True)
+                S = 33 * ELEM[dt]
+                L = (n - 1).bit_length()
+                assert sum(sent) == 2 * (n - 1) * S
+                assert sent[0] == L * S, (n, sent)
+                assert all(sent[r] == S for r in range(1, n, 2)), (n, sent)
+                for r in range(1, n):
+                    assert same_bits(tree[r], tree[0]), (n, dt, op)
+                ring = o.fold_all_reduce(xs, dt, op)[0]
+                if dt == "i32" or op in ("max", "min"):
+                    assert same_bits(tree[0], ring), (n, dt, op)
+                elif op in ("sum", "avg"):
+                    x64 = np.stack([to_f64(a, dt) for a in xs])
+                    absum = np.abs(x64).sum(axis=0) / (n if op == "avg" else 1)
+                    exact = np.array([math.fsum(x64[:, i]) for i in range(33)]) / (n if op == "avg" else 1)
+                    ulp = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[dt]
+                    y = to_f64(tree[0], dt)
+                    bound = _gamma(L, 2.0 ** -24) * absum * 1.01 + (ulp + 2.0 ** -24) * np.abs(y) + 1e-30
+                    assert np.all(np.abs(y - exact) <= bound), (n, dt, op)
+                    tol = 4 * n * eps * absum + 2 * ulp * np.abs(y) + 1e-30
+                    assert np.all(np.abs(y - to_f64(ring, dt)) <= tol), (n, dt, op)
+
+
 ALL_PINS = [
     pin_worked_example, pin_bytes_sent_page, pin_bytes_closed_form, pin_partition_torch_chunk,
     pin_ring_order, pin_fp32_accumulate, pin_forms_agree, pin_int_brute_force, pin_fp_maxmin,
     pin_sum_error_bound, pin_avg_pow2, pin_prod_bound, pin_f16_conversions, pin_bf16_conversions,
     pin_rs_ag_equals_ar, pin_all_gather_concat, pin_elements_match, pin_all_to_all,
+    pin_tree,
 ]
 
 

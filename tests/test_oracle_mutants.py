@@ -51,6 +51,13 @@ MUTANTS = [
     ("alltoall_transposed_wrong", "memcpy((unsigned char*)out[p] + (size_t)r * blk, (const unsigned char*)in[r] + (size_t)p * blk, blk);",
      "memcpy((unsigned char*)out[p] + (size_t)p * blk, (const unsigned char*)in[r] + (size_t)r * blk, blk);"),
     ("alltoall_counts_own_block", "if (sent && p != r) sent[r] += blk;", "if (sent) sent[r] += blk;"),
+    ("tree_pairs_wrong_partner", "int q = r + stride;", "int q = r + stride / 2 + (stride == 1);"),
+    ("tree_no_broadcast_count", "memcpy(out[r + stride], out[r], bytes);\n            if (sent) sent[r] += bytes;",
+     "memcpy(out[r + stride], out[r], bytes);"),
+    ("tree_sequential_order", "for (uint64_t i = 0; i < count; i++) W[r][i] = combine(dtype, op, W[r][i], W[q][i]);",
+     "for (uint64_t i = 0; i < count; i++) W[r][i] = combine(dtype, op, W[r][i], W[q][i]);\n"
+     "            if (r == 0 && stride == 1) for (int k = 2; k < n; k++) for (uint64_t i = 0; i < count; i++) W[0][i] = combine(dtype, op, W[0][i], W[k][i]);\n"
+     "            if (r == 0 && stride == 1) { stride = n; break; }"),
     ("allgather_block_order", "memmove((unsigned char*)out[r] + (size_t)r * blk, in[r], blk);",
      "memmove((unsigned char*)out[r] + (size_t)((r + 1) % n) * blk, in[r], blk);"),
 ]
