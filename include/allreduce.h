@@ -91,7 +91,24 @@ typedef enum { AR_SUM = 0, AR_AVG = 1, AR_MAX = 2, AR_MIN = 3, AR_PROD = 4 } ar_
  * is itself being captured (INVALID_ARGUMENT): capture AR_MODE_RING_STEPWISE
  * or AR_MODE_FUSED instead -- both are capture-safe (no synchronous calls,
  * no memsets, no allocation). Same bits as the other modes. */
-typedef enum { AR_MODE_FUSED = 0, AR_MODE_RING_STEPWISE = 1, AR_MODE_RING_GRAPH = 2 } ar_mode_t;
+/* AR_MODE_TREE and AR_MODE_TREE_STEPWISE (all-reduce only; other
+ * collectives return UNSUPPORTED): the tree variant [P3 section 六]. Ranks
+ * combine in pairs, the pair results combine in pairs again, and after
+ * ceil(log2 N) levels rank 0 holds the reduction, which is broadcast back
+ * down: level l pairs rank r (a multiple of 2^(l+1)) with r + 2^l. Every
+ * element is folded in that order (no chunks), so for fp SUM/AVG/PROD the
+ * bits differ from the ring's; the difference is bounded by
+ * 4*N*eps*sum|x_i| (eps = 2^-23, plus one output ulp for fp16/bf16).
+ * AR_MODE_TREE: one launch, each element's tree evaluated in registers.
+ * AR_MODE_TREE_STEPWISE: 2*ceil(log2 N) launches (the pages' step count);
+ * fp16/bf16 partials need ar_workspace_bytes(...) of fp32 workspace. */
+typedef enum {
+    AR_MODE_FUSED = 0,
+    AR_MODE_RING_STEPWISE = 1,
+    AR_MODE_RING_GRAPH = 2,
+    AR_MODE_TREE = 3,
+    AR_MODE_TREE_STEPWISE = 4
+} ar_mode_t;
 
 typedef enum {
     AR_COLL_ALL_REDUCE = 0,
@@ -118,7 +135,9 @@ int ar_comm_nranks(ar_comm_t comm);
  * collective's own count argument (count, recvcount or sendcount).
  * The ring modes (stepwise and graph) need it: all-reduce of fp16/bf16
  * keeps fp32 partial sums, 4*count bytes; reduce-scatter keeps the partials
- * of all nranks blocks, 4*nranks*recvcount bytes. Everything else: 0. Returns (size_t)-1 for
+ * of all nranks blocks, 4*nranks*recvcount bytes. AR_MODE_TREE_STEPWISE
+ * with fp16/bf16 keeps floor(N/2) fp32 partial buffers:
+ * 4*floor(N/2)*roundup(count, 4) bytes. Everything else: 0. Returns (size_t)-1 for
  * invalid arguments or if the size overflows. */
 size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype, ar_mode_t mode);
 

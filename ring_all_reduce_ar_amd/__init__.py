@@ -39,13 +39,14 @@ AR_FLOAT32, AR_FLOAT16, AR_BFLOAT16, AR_INT32 = range(4)
 # ar_op_t
 AR_SUM, AR_AVG, AR_MAX, AR_MIN, AR_PROD = range(5)
 # ar_mode_t
-AR_MODE_FUSED, AR_MODE_RING_STEPWISE, AR_MODE_RING_GRAPH = range(3)
+AR_MODE_FUSED, AR_MODE_RING_STEPWISE, AR_MODE_RING_GRAPH, AR_MODE_TREE, AR_MODE_TREE_STEPWISE = range(5)
 # ar_collective_t
 AR_COLL_ALL_REDUCE, AR_COLL_REDUCE_SCATTER, AR_COLL_ALL_GATHER, AR_COLL_ALL_TO_ALL = range(4)
 
 DTYPE_NAMES = {"f32": AR_FLOAT32, "f16": AR_FLOAT16, "bf16": AR_BFLOAT16, "i32": AR_INT32}
 OP_NAMES = {"sum": AR_SUM, "avg": AR_AVG, "max": AR_MAX, "min": AR_MIN, "prod": AR_PROD}
-MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph": AR_MODE_RING_GRAPH}
+MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph": AR_MODE_RING_GRAPH,
+              "tree": AR_MODE_TREE, "tree_stepwise": AR_MODE_TREE_STEPWISE}
 
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",

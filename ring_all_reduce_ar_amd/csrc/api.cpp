@@ -75,7 +75,8 @@ size_t elem_size(ar_dtype_t d)
 
 bool valid_dtype(int d) { return d >= AR_FLOAT32 && d <= AR_INT32; }
 bool valid_op(int o) { return o >= AR_SUM && o <= AR_PROD; }
-bool valid_mode(int m) { return m == AR_MODE_FUSED || m == AR_MODE_RING_STEPWISE || m == AR_MODE_RING_GRAPH; }
+bool valid_mode(int m) { return m >= AR_MODE_FUSED && m <= AR_MODE_TREE_STEPWISE; }
+bool tree_mode(int m) { return m == AR_MODE_TREE || m == AR_MODE_TREE_STEPWISE; }
 
 const char* dtype_name(ar_dtype_t d)
 {
@@ -287,10 +288,21 @@ AR_EXPORT int ar_comm_nranks(ar_comm_t comm) { return comm ? comm->nranks : -1; 
 AR_EXPORT size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t count, ar_dtype_t dtype, ar_mode_t mode)
 {
     if (nranks < 1 || nranks > AR_MAX_RANKS || !valid_dtype(dtype) || !valid_mode(mode)) return static_cast<size_t>(-1);
-    if ((mode != AR_MODE_RING_STEPWISE && mode != AR_MODE_RING_GRAPH) || nranks == 1) return 0;
+    if (coll < AR_COLL_ALL_REDUCE || coll > AR_COLL_ALL_TO_ALL) return static_cast<size_t>(-1);
+    if (nranks == 1) return 0;
+    const bool half = dtype == AR_FLOAT16 || dtype == AR_BFLOAT16;
     size_t out = 0;
+    if (mode == AR_MODE_TREE_STEPWISE) {
+        if (coll != AR_COLL_ALL_REDUCE || !half) return 0;
+        if (count > SIZE_MAX - 3) return static_cast<size_t>(-1);
+        size_t slots = 0;
+        if (!mul_ok((count + 3) / 4 * 4, static_cast<size_t>(nranks / 2), &slots) || !mul_ok(slots, 4, &out))
+            return static_cast<size_t>(-1);
+        return out;
+    }
+    if (mode != AR_MODE_RING_STEPWISE && mode != AR_MODE_RING_GRAPH) return 0;
     if (coll == AR_COLL_ALL_REDUCE) {
-        if (dtype != AR_FLOAT16 && dtype != AR_BFLOAT16) return 0;
+        if (!half) return 0;
         return mul_ok(count, 4, &out) ? out : static_cast<size_t>(-1);
     }
     if (coll == AR_COLL_REDUCE_SCATTER) {
@@ -299,8 +311,7 @@ AR_EXPORT size_t ar_workspace_bytes(ar_collective_t coll, int nranks, size_t cou
             return static_cast<size_t>(-1);
         return out;
     }
-    if (coll == AR_COLL_ALL_GATHER) return 0;
-    return static_cast<size_t>(-1);
+    return 0;
 }
 
 AR_EXPORT ar_result_t ar_comm_set_workspace(ar_comm_t comm, void* dev_ptr, size_t bytes)
@@ -436,6 +447,65 @@ bool ring_mode(ar_mode_t mode) { return mode == AR_MODE_RING_STEPWISE || mode ==
 
 }  // namespace
 
+namespace {
+
+// The tree variant: a fused single pass in tree order, or 2*ceil(log2 n)
+// level launches (reduce up to rank 0, broadcast back down).
+ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
+                            ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
+{
+    const int n = comm->nranks;
+    const size_t e = elem_size(dtype);
+    const uint64_t epv = 16 / e;
+    const bool aligned = all_aligned16(n, sendbufs, recvbufs);
+    DeviceGuard g(comm->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    if (comm->debug)
+        std::fprintf(stderr, "[allreduce] all_reduce tree n=%d count=%zu dtype=%s op=%d mode=%d vec=%d\n", n, count,
+                     dtype_name(dtype), static_cast<int>(op), static_cast<int>(mode), aligned ? 1 : 0);
+    if (mode == AR_MODE_TREE) {
+        ar::ReduceArgs a{};
+        fill_ptrs(a, n, sendbufs, recvbufs);
+        a.count = count;
+        a.q = count;
+        a.n = n;
+        const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, fused_per_cu(count * e));
+        return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
+            hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, gx, s);
+            return err != hipSuccess ? err : tick(t);
+        });
+    }
+    int levels = 0;
+    while ((1 << levels) < n) ++levels;
+    ar::TreeArgs ta{};
+    fill_ptrs(ta, n, sendbufs, recvbufs);
+    ta.ws = (dtype == AR_FLOAT16 || dtype == AR_BFLOAT16) ? comm->ws : nullptr;
+    ta.ws_stride = (count + 3) / 4 * 4;
+    ta.count = count;
+    ta.n = n;
+    const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, std::max(1, n / 2));
+    const bool bvec = aligned;
+    Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
+        for (int l = 0; l < levels; ++l) {
+            ta.stride = 1 << l;
+            ta.last = l == levels - 1;
+            hipError_t err = ar::launch_tree_reduce_level(ta, dtype, op, aligned, gx, s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        for (int l = levels - 1; l >= 0; --l) {
+            ta.stride = 1 << l;
+            hipError_t err = ar::launch_tree_bcast_level(ta, e, bvec, gx, s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    };
+    return run_eager(comm, stream, 2 * levels, fn);
+}
+
+}  // namespace
+
 AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
                                     ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
 {
@@ -448,12 +518,13 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     if (!mul_ok(count, e, &bytes)) return fail(AR_ERR_INVALID_ARGUMENT, "count %zu overflows", count);
     if (count == 0) return AR_SUCCESS;
     const bool stepwise = ring_mode(mode) && n > 1;
-    const size_t ws_need = stepwise ? ar_workspace_bytes(AR_COLL_ALL_REDUCE, n, count, dtype, mode) : 0;
+    const size_t ws_need = ar_workspace_bytes(AR_COLL_ALL_REDUCE, n, count, dtype, mode);
     if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
     rc = need_workspace(comm, ws_need);
     if (rc != AR_SUCCESS) return rc;
     rc = check_buffers(n, sendbufs, recvbufs, bytes, bytes, AR_COLL_ALL_REDUCE, e, comm->ws, ws_need);
     if (rc != AR_SUCCESS) return rc;
+    if (tree_mode(mode) && n > 1) return tree_all_reduce(comm, sendbufs, recvbufs, count, dtype, op, mode, stream);
 
     // Ring plan: q = ceil(count / n); chunk c = [c*q, min((c+1)*q, count)).
     const uint64_t q = ceil_div(count, static_cast<uint64_t>(n));
@@ -527,6 +598,8 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
 {
     ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
     if (rc != AR_SUCCESS) return rc;
+    if (tree_mode(mode))
+        return fail(AR_ERR_UNSUPPORTED, "the tree modes are defined for all-reduce only");
     if (!valid_op(op)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid op %d", static_cast<int>(op));
     const int n = comm->nranks;
     const size_t e = elem_size(dtype);
@@ -594,6 +667,8 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
 {
     ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
     if (rc != AR_SUCCESS) return rc;
+    if (tree_mode(mode))
+        return fail(AR_ERR_UNSUPPORTED, "the tree modes are defined for all-reduce only");
     const int n = comm->nranks;
     const size_t e = elem_size(dtype);
     size_t blk = 0, rbytes = 0;
@@ -666,6 +741,8 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
 {
     ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
     if (rc != AR_SUCCESS) return rc;
+    if (tree_mode(mode))
+        return fail(AR_ERR_UNSUPPORTED, "the tree modes are defined for all-reduce only");
     const int n = comm->nranks;
     const size_t e = elem_size(dtype);
     size_t blk = 0, total = 0;

@@ -54,6 +54,27 @@ struct CopyArgs {
     int shift;
 };
 
+// One level of the tree variant. Reduce level (stride s = 2^l): for every
+// pair (r, q = r + s) with r a multiple of 2s, r combines local (+)
+// incoming; partials live in recv (fp32/int32) or in fp32 workspace slot r/2
+// (fp16/bf16). Broadcast level: recv[q] = recv[r]. Grid row j is pair j.
+struct TreeArgs {
+    const void* send[AR_MAX_RANKS];
+    void* recv[AR_MAX_RANKS];
+    void* ws;
+    uint64_t ws_stride;  // elements per workspace slot: count rounded up to a multiple of 4
+    uint64_t count;
+    int n;
+    int stride;
+    int last;  // the root's final level: finalize (AVG, rounding) into recv[0]
+};
+
+hipError_t launch_tree_fused(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
+                             hipStream_t stream);
+hipError_t launch_tree_reduce_level(const TreeArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
+                                    hipStream_t stream);
+hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int grid_x, hipStream_t stream);
+
 // All-to-all block copies: row y copies block p of send[r] to block r of
 // recv[p], `blk` bytes. step < 0: all n*n (r, p) pairs, row y = r*n + p;
 // step s >= 0: the n pairs (r, (r + s) mod n), row y = r.

@@ -519,6 +519,225 @@ __global__ __launch_bounds__(kBlock) void local_copy(const CopyArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// tree variant [geek-doc "训练梯度同步与集合通信", section 六]: ranks combine
+// in pairs, pair results combine in pairs again, the root ends with the
+// reduction, which goes back down the tree. For element i the fold is the
+// binomial tree over ranks 0..n-1: T(lo, hi) = T(lo, lo+P) (+) T(lo+P, hi),
+// P the largest power of two below hi-lo. One thread evaluates it with a
+// binary counter: slot[b] holds the partial of an aligned block of 2^b ranks;
+// adding rank r carries through the slots whose bit is set in r (the lower
+// ranks' block is the left operand), and the slots left at the end (the set
+// bits of n) fold from the smallest block upward.
+// ---------------------------------------------------------------------------
+constexpr int kTreeSlots = 7;  // 2^6 = AR_MAX_RANKS
+
+template <class F, int OP, int NR>
+__device__ __forceinline__ void tree_fold_vec(const ReduceArgs& a, int n, uint64_t vi, typename F::Acc* out)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    constexpr int RMAX = NR > 0 ? NR : AR_MAX_RANKS;
+    Acc slot[kTreeSlots][E];
+#pragma unroll
+    for (int rb = 0; rb < RMAX; rb += 8) {
+        if (NR > 0 || rb < n) {
+            u32x4 x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (rb + j < RMAX) x[j] = ld16_nt(a.send[min(rb + j, n - 1)], vi);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = rb + j;  // compile-time after unrolling
+                if (r < RMAX && (NR > 0 || r < n)) {
+                    Acc carry[E];
+                    F::unpack(x[j], carry);
+                    int b = 0;
+#pragma unroll
+                    for (; b < kTreeSlots - 1; ++b) {
+                        if (!((r >> b) & 1)) break;
+#pragma unroll
+                        for (int e = 0; e < E; ++e) carry[e] = combine<OP>(slot[b][e], carry[e]);
+                    }
+#pragma unroll
+                    for (int e = 0; e < E; ++e) slot[b][e] = carry[e];
+                }
+            }
+        }
+    }
+    bool have = false;
+#pragma unroll
+    for (int b = 0; b < kTreeSlots; ++b) {
+        if ((n >> b) & 1) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) out[e] = have ? combine<OP>(slot[b][e], out[e]) : slot[b][e];
+            have = true;
+        }
+    }
+}
+
+template <class F, int OP>
+__device__ __forceinline__ typename F::Acc tree_fold_elem(const ReduceArgs& a, int n, uint64_t i)
+{
+    using Acc = typename F::Acc;
+    Acc slot[kTreeSlots];
+#pragma unroll
+    for (int r = 0; r < AR_MAX_RANKS; ++r) {
+        if (r < n) {
+            Acc carry = F::ld(a.send[r], i);
+            int b = 0;
+#pragma unroll
+            for (; b < kTreeSlots - 1; ++b) {
+                if (!((r >> b) & 1)) break;
+                carry = combine<OP>(slot[b], carry);
+            }
+            slot[b] = carry;
+        }
+    }
+    Acc out{};
+    bool have = false;
+#pragma unroll
+    for (int b = 0; b < kTreeSlots; ++b) {
+        if ((n >> b) & 1) {
+            out = have ? combine<OP>(slot[b], out) : slot[b];
+            have = true;
+        }
+    }
+    return out;
+}
+
+// Fused tree all-reduce: 1-D grid-stride over 16-byte vectors of the whole
+// buffer; every element takes the same tree order.
+template <class F, int OP, int NR>
+__global__ __launch_bounds__(kBlock) void tree_fused_vec(const ReduceArgs a)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const int n = NR > 0 ? NR : a.n;
+    const uint64_t nv = a.count / E;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t v = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; v < nv; v += stride) {
+        Acc acc[E];
+        tree_fold_vec<F, OP, NR>(a, n, v, acc);
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
+        const u32x4 out = F::pack(acc);
+        for (int r = 0; r < n; ++r) st16_nt(a.recv[r], v, out);
+    }
+    if (blockIdx.x == 0) {
+        const uint64_t i = nv * E + threadIdx.x;
+        if (i < a.count) {
+            const Acc x = finalize<OP>(tree_fold_elem<F, OP>(a, n, i), n);
+            for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
+        }
+    }
+}
+
+template <class F, int OP>
+__global__ __launch_bounds__(kBlock) void tree_fused_scalar(const ReduceArgs a)
+{
+    const int n = a.n;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < a.count; i += stride) {
+        const typename F::Acc x = finalize<OP>(tree_fold_elem<F, OP>(a, n, i), n);
+        for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
+    }
+}
+
+// Partial of rank x in the stepwise tree: recv[x] for fp32/int32 (storage =
+// accumulator), fp32 workspace slot x/2 for fp16/bf16.
+template <class F>
+__device__ __forceinline__ typename F::Acc tree_partial_ld(const TreeArgs& a, int x, uint64_t i)
+{
+    typename F::Acc v;
+    if (a.ws) from_bits(static_cast<const uint32_t*>(a.ws)[static_cast<uint64_t>(x / 2) * a.ws_stride + i], v);
+    else v = F::ld(a.recv[x], i);
+    return v;
+}
+
+template <class F>
+__device__ __forceinline__ void tree_partial_st(const TreeArgs& a, int x, uint64_t i, typename F::Acc v)
+{
+    if (a.ws) static_cast<uint32_t*>(a.ws)[static_cast<uint64_t>(x / 2) * a.ws_stride + i] = to_bits(v);
+    else F::st(a.recv[x], i, v);
+}
+
+template <class F, int OP>
+__device__ __forceinline__ void tree_reduce_elem(const TreeArgs& a, int r, int q, uint64_t i)
+{
+    using Acc = typename F::Acc;
+    // A rank holds a partial once it has received at level 0, i.e. when it
+    // is even and has a right neighbour; r always has, q only if q+1 < n.
+    const Acc local = a.stride == 1 ? F::ld(a.send[r], i) : tree_partial_ld<F>(a, r, i);
+    const Acc in = (a.stride == 1 || q + 1 >= a.n) ? F::ld(a.send[q], i) : tree_partial_ld<F>(a, q, i);
+    Acc v = combine<OP>(local, in);
+    if (a.last) F::st(a.recv[0], i, finalize<OP>(v, a.n));
+    else tree_partial_st<F>(a, r, i, v);
+}
+
+template <class F, int OP, bool VEC>
+__global__ __launch_bounds__(kBlock) void tree_reduce_level(const TreeArgs a)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const int r = blockIdx.y * 2 * a.stride;
+    const int q = r + a.stride;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if constexpr (VEC) {
+        const uint64_t nv = a.count / E;
+        const bool local_partial = a.stride != 1, in_partial = a.stride != 1 && q + 1 < a.n;
+        for (uint64_t v = t0; v < nv; v += stride) {
+            Acc loc[E], in[E];
+            if (!local_partial) F::unpack(ld16(a.send[r], v), loc);
+            else if (a.ws) ws_load<F>(static_cast<const uint32_t*>(a.ws) + static_cast<uint64_t>(r / 2) * a.ws_stride, v * E, loc);
+            else F::unpack(ld16(a.recv[r], v), loc);
+            if (!in_partial) F::unpack(ld16(a.send[q], v), in);
+            else if (a.ws) ws_load<F>(static_cast<const uint32_t*>(a.ws) + static_cast<uint64_t>(q / 2) * a.ws_stride, v * E, in);
+            else F::unpack(ld16(a.recv[q], v), in);
+#pragma unroll
+            for (int j = 0; j < E; ++j) loc[j] = combine<OP>(loc[j], in[j]);
+            if (a.last) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) loc[j] = finalize<OP>(loc[j], a.n);
+                st16(a.recv[0], v, F::pack(loc));
+            } else if (a.ws) {
+                ws_store<F>(static_cast<uint32_t*>(a.ws) + static_cast<uint64_t>(r / 2) * a.ws_stride, v * E, loc);
+            } else {
+                st16(a.recv[r], v, F::pack(loc));
+            }
+        }
+        if (blockIdx.x == 0 && nv * E + threadIdx.x < a.count) tree_reduce_elem<F, OP>(a, r, q, nv * E + threadIdx.x);
+    } else {
+        for (uint64_t i = t0; i < a.count; i += stride) tree_reduce_elem<F, OP>(a, r, q, i);
+    }
+}
+
+// Broadcast level: recv[q] = recv[r], count*elem bytes.
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void tree_bcast_level(const TreeArgs a, uint64_t bytes)
+{
+    const int r = blockIdx.y * 2 * a.stride;
+    const int q = r + a.stride;
+    const char* src = static_cast<const char*>(a.recv[r]);
+    char* dst = static_cast<char*>(a.recv[q]);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
+    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    uint64_t done = 0;
+    if constexpr (VEC) {
+        const uint64_t nv = bytes / 16;
+        for (uint64_t v = t0; v < nv; v += stride) st16_nt(dst, v, ld16(src, v));
+        done = nv * 16;
+        if (blockIdx.x != 0) return;
+        for (uint64_t b = done + 2 * threadIdx.x; b < bytes; b += 2 * kBlock)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    } else {
+        for (uint64_t b = 2 * t0; b < bytes; b += 2 * stride)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // all-to-all [handbook "集合通信原语", section 五个原语]: rank r's block p
 // becomes rank p's block r
 // ---------------------------------------------------------------------------
@@ -617,6 +836,92 @@ hipError_t rs_op(const StepArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t
     return hipErrorInvalidValue;
 }
 
+template <class F, int OP>
+hipError_t tree_n(const ReduceArgs& a, bool vec, dim3 grid, hipStream_t s)
+{
+    const dim3 block(kBlock);
+    if (!vec) hipLaunchKernelGGL((tree_fused_scalar<F, OP>), grid, block, 0, s, a);
+    else if (a.n == 2) hipLaunchKernelGGL((tree_fused_vec<F, OP, 2>), grid, block, 0, s, a);
+    else if (a.n == 4) hipLaunchKernelGGL((tree_fused_vec<F, OP, 4>), grid, block, 0, s, a);
+    else if (a.n == 8) hipLaunchKernelGGL((tree_fused_vec<F, OP, 8>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((tree_fused_vec<F, OP, 0>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <class F>
+hipError_t tree_op(const ReduceArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+{
+    switch (op) {
+    case AR_SUM: return tree_n<F, AR_SUM>(a, vec, grid, s);
+    case AR_AVG: return tree_n<F, AR_AVG>(a, vec, grid, s);
+    case AR_MAX: return tree_n<F, AR_MAX>(a, vec, grid, s);
+    case AR_MIN: return tree_n<F, AR_MIN>(a, vec, grid, s);
+    case AR_PROD: return tree_n<F, AR_PROD>(a, vec, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class F, int OP>
+hipError_t tree_level_vec(const TreeArgs& a, bool vec, dim3 grid, hipStream_t s)
+{
+    if (vec) hipLaunchKernelGGL((tree_reduce_level<F, OP, true>), grid, dim3(kBlock), 0, s, a);
+    else hipLaunchKernelGGL((tree_reduce_level<F, OP, false>), grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class F>
+hipError_t tree_level_op(const TreeArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+{
+    switch (op) {
+    case AR_SUM: return tree_level_vec<F, AR_SUM>(a, vec, grid, s);
+    case AR_AVG: return tree_level_vec<F, AR_AVG>(a, vec, grid, s);
+    case AR_MAX: return tree_level_vec<F, AR_MAX>(a, vec, grid, s);
+    case AR_MIN: return tree_level_vec<F, AR_MIN>(a, vec, grid, s);
+    case AR_PROD: return tree_level_vec<F, AR_PROD>(a, vec, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int tree_pairs(int n, int stride) { return n > stride ? (n - stride - 1) / (2 * stride) + 1 : 0; }
+
+hipError_t launch_tree_fused(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
+                             hipStream_t stream)
+{
+    const dim3 grid(grid_x);
+    switch (dtype) {
+    case AR_FLOAT32: return tree_op<F32>(a, op, vec, grid, stream);
+    case AR_FLOAT16: return tree_op<F16>(a, op, vec, grid, stream);
+    case AR_BFLOAT16: return tree_op<BF16>(a, op, vec, grid, stream);
+    case AR_INT32: return tree_op<I32>(a, op, vec, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_tree_reduce_level(const TreeArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
+                                    hipStream_t stream)
+{
+    const dim3 grid(grid_x, tree_pairs(a.n, a.stride));
+    switch (dtype) {
+    case AR_FLOAT32: return tree_level_op<F32>(a, op, vec, grid, stream);
+    case AR_FLOAT16: return tree_level_op<F16>(a, op, vec, grid, stream);
+    case AR_BFLOAT16: return tree_level_op<BF16>(a, op, vec, grid, stream);
+    case AR_INT32: return tree_level_op<I32>(a, op, vec, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int grid_x, hipStream_t stream)
+{
+    const dim3 grid(grid_x, tree_pairs(a.n, a.stride));
+    const uint64_t bytes = a.count * elem;
+    if (vec) hipLaunchKernelGGL((tree_bcast_level<true>), grid, dim3(kBlock), 0, stream, a, bytes);
+    else hipLaunchKernelGGL((tree_bcast_level<false>), grid, dim3(kBlock), 0, stream, a, bytes);
+    return hipGetLastError();
+}
+
+namespace {
 }  // namespace
 
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, int grid_x,
