@@ -51,6 +51,7 @@ extern "C" {
 #endif
 
 #define AR_MAX_RANKS 64
+#define AR_MAX_TENSORS 65536
 
 typedef struct ar_comm* ar_comm_t;
 
@@ -192,6 +193,24 @@ ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[], void* co
  * all (there is no in-place form); errors otherwise as ar_all_reduce. */
 ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t blockcount,
                           ar_dtype_t dtype, ar_mode_t mode, hipStream_t stream);
+
+/* Coalesced multi-tensor all-reduce: many gradient tensors reduced in one
+ * call without packing them into a bucket first -- the pages' gradient
+ * bucketing and small-tensor fusion [P1 s5.1-s5.2 (DDP buckets, default
+ * 25 MB); P2 s5.3 (merge same-shape gradients into one call); P3 section 四
+ * (fuse small tensors so the per-step latency is paid once)].
+ * Tensor t of rank r is sendbufs[t*nranks + r] / recvbufs[t*nranks + r]
+ * with counts[t] elements (t < ntensors <= AR_MAX_TENSORS; empty tensors
+ * allowed). The tensors of a rank form one virtual flat bucket, in tensor
+ * order; the ring's chunks are taken over that bucket, so every element gets
+ * exactly the bits ar_all_reduce gives on the packed bucket. Each tensor may
+ * be in place (send == recv); any other overlap is INVALID_ARGUMENT.
+ * AR_MODE_FUSED only (other modes: UNSUPPORTED). Launches: one per batch of
+ * tensors whose rank pointers fit the kernel arguments (about 3.8 KB: e.g.
+ * 24 tensors per launch at 8 ranks, 3 at 64). No workspace. */
+ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const void* const sendbufs[], void* const recvbufs[],
+                                const size_t counts[], ar_dtype_t dtype, ar_op_t op, ar_mode_t mode,
+                                hipStream_t stream);
 
 /* Per-step timing of stepwise calls (the alpha-beta model's per-step cost,
  * [P3 section 四; P4 section α-β 模型]). When enabled, each stepwise call

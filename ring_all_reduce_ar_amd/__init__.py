@@ -50,8 +50,8 @@ MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph"
 
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",
-    "ar_all_reduce", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_comm_set_step_timing",
-    "ar_last_step_times_ms",
+    "ar_all_reduce", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi",
+    "ar_comm_set_step_timing", "ar_last_step_times_ms",
     "ar_result_string", "ar_last_error",
 )
 
@@ -69,6 +69,8 @@ _lib.ar_all_reduce.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_
 _lib.ar_reduce_scatter.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _c_int, _vp]
 _lib.ar_all_gather.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _vp]
 _lib.ar_all_to_all.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _vp]
+_lib.ar_all_reduce_multi.argtypes = [_vp, _c_int, _ptr_array, _ptr_array, ctypes.POINTER(_c_size), _c_int, _c_int,
+                                     _c_int, _vp]
 _lib.ar_comm_set_step_timing.argtypes = [_vp, _c_int]
 _lib.ar_last_step_times_ms.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]
 _lib.ar_result_string.argtypes = [_c_int]
@@ -76,7 +78,8 @@ _lib.ar_result_string.restype = ctypes.c_char_p
 _lib.ar_last_error.argtypes = []
 _lib.ar_last_error.restype = ctypes.c_char_p
 for _name in ("ar_comm_create", "ar_comm_destroy", "ar_comm_set_workspace", "ar_all_reduce", "ar_reduce_scatter",
-              "ar_all_gather", "ar_all_to_all", "ar_comm_set_step_timing", "ar_last_step_times_ms"):
+              "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi", "ar_comm_set_step_timing",
+              "ar_last_step_times_ms"):
     getattr(_lib, _name).restype = _c_int
 
 
@@ -224,6 +227,19 @@ def ar_all_to_all(comm, sendbufs, recvbufs, blockcount: int, dtype, mode="fused"
     _check(_lib.ar_all_to_all(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), blockcount,
                               _enum(dtype, DTYPE_NAMES, "dtype"), _enum(mode, MODE_NAMES, "mode"),
                               _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_to_all")
+
+
+def ar_all_reduce_multi(comm, sendbufs, recvbufs, counts, dtype, op, mode="fused", stream=None):
+    """sendbufs / recvbufs: one list of per-rank buffers per tensor
+    (``sendbufs[t][r]``), or a flat tensor-major list; counts[t] elements."""
+    nt = len(counts)
+    flat_s = [b for row in sendbufs for b in row] if nt and isinstance(sendbufs[0], (list, tuple)) else list(sendbufs)
+    flat_r = [b for row in recvbufs for b in row] if nt and isinstance(recvbufs[0], (list, tuple)) else list(recvbufs)
+    arr = (ctypes.c_size_t * max(nt, 1))(*counts)
+    _check(_lib.ar_all_reduce_multi(_h(comm), nt, _ptrs(flat_s), _ptrs(flat_r), arr, _enum(dtype, DTYPE_NAMES, "dtype"),
+                                    _enum(op, OP_NAMES, "op"), _enum(mode, MODE_NAMES, "mode"),
+                                    _stream(stream, comm.device if isinstance(comm, Comm) else 0)),
+           "ar_all_reduce_multi")
 
 
 def ar_comm_set_step_timing(comm, enable: bool):

@@ -787,6 +787,145 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
     return run_eager(comm, stream, n, fn);
 }
 
+// Coalesced multi-tensor all-reduce: tensor t of rank r is
+// sendbufs[t*n + r] / recvbufs[t*n + r] with counts[t] elements. The tensors
+// of a rank are one virtual flat bucket in tensor order, partitioned into
+// ring chunks as one buffer.
+AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const void* const sendbufs[],
+                                          void* const recvbufs[], const size_t counts[], ar_dtype_t dtype, ar_op_t op,
+                                          ar_mode_t mode, hipStream_t stream)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
+    if (ntensors < 0 || ntensors > AR_MAX_TENSORS)
+        return fail(AR_ERR_INVALID_ARGUMENT, "ntensors %d is outside 0..%d", ntensors, AR_MAX_TENSORS);
+    if (ntensors > 0 && (!sendbufs || !recvbufs || !counts))
+        return fail(AR_ERR_INVALID_ARGUMENT, "NULL sendbufs, recvbufs or counts array");
+    if (!valid_dtype(dtype)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid dtype %d", static_cast<int>(dtype));
+    if (!valid_op(op)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid op %d", static_cast<int>(op));
+    if (!valid_mode(mode)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid mode %d", static_cast<int>(mode));
+    if (mode != AR_MODE_FUSED)
+        return fail(AR_ERR_UNSUPPORTED, "the multi-tensor all-reduce runs in AR_MODE_FUSED only");
+    const int n = comm->nranks;
+    const size_t e = elem_size(dtype);
+    uint64_t total = 0;
+    std::vector<Interval> iv;
+    for (int t = 0; t < ntensors; ++t) {
+        size_t bytes = 0;
+        if (!mul_ok(counts[t], e, &bytes) || total + counts[t] < total)
+            return fail(AR_ERR_INVALID_ARGUMENT, "counts[%d] = %zu overflows", t, counts[t]);
+        total += counts[t];
+        if (counts[t] == 0) continue;
+        for (int r = 0; r < n; ++r) {
+            const void* sp = sendbufs[static_cast<size_t>(t) * n + r];
+            const void* dp = recvbufs[static_cast<size_t>(t) * n + r];
+            if (!sp || !dp) return fail(AR_ERR_INVALID_ARGUMENT, "tensor %d rank %d buffer is NULL", t, r);
+            const uintptr_t s = reinterpret_cast<uintptr_t>(sp), d = reinterpret_cast<uintptr_t>(dp);
+            if (s % e || d % e)
+                return fail(AR_ERR_INVALID_ARGUMENT, "tensor %d rank %d buffer is not aligned to %zu bytes", t, r, e);
+            if (s > UINTPTR_MAX - bytes || d > UINTPTR_MAX - bytes)
+                return fail(AR_ERR_INVALID_ARGUMENT, "tensor %d rank %d buffer wraps the address space", t, r);
+            if (s == d) {
+                iv.push_back({s, s + bytes, "in-place tensor", t});
+            } else {
+                iv.push_back({s, s + bytes, "send tensor", t});
+                iv.push_back({d, d + bytes, "recv tensor", t});
+            }
+        }
+    }
+    if (total == 0) return AR_SUCCESS;
+    std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < iv.size(); ++i)
+        if (iv[i].lo < iv[i - 1].hi)
+            return fail(AR_ERR_INVALID_ARGUMENT, "%s %d overlaps %s %d (only send == recv may alias)", iv[i].what,
+                        iv[i].rank, iv[i - 1].what, iv[i - 1].rank);
+
+    DeviceGuard g(comm->device);
+    if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+    const uint64_t q = ceil_div(total, static_cast<uint64_t>(n));
+    const uint64_t E = 16 / e;
+    const size_t ptr_block = static_cast<size_t>(2 * n) * sizeof(void*);
+
+    // Plan the batches: consecutive tensors whose pointer blocks and pieces
+    // fit the kernel-argument blob.
+    std::vector<ar::MultiArgs> batches;
+    ar::MultiArgs cur{};
+    int cur_tensors = 0;
+    std::vector<ar::MultiPiece> cur_pieces;
+    std::vector<std::vector<const void*>> cur_ptrs;
+    auto flush = [&]() {
+        if (cur_tensors == 0) return;
+        ar::MultiArgs a{};
+        a.n = n;
+        a.npieces = static_cast<int>(cur_pieces.size());
+        a.pieces_offset = static_cast<uint32_t>(cur_tensors * ptr_block);
+        uint32_t tiles = 0;
+        for (auto& pc : cur_pieces) {
+            pc.tile0 = tiles;
+            uint64_t nt;
+            if (pc.vec) {
+                const uint64_t vb = (pc.j0 + E - 1) / E, ve = (pc.j0 + pc.len) / E;
+                nt = std::max<uint64_t>(1, ve > vb ? ceil_div(ve - vb, ar::kBlock) : 0);
+            } else {
+                nt = ceil_div(pc.len, ar::kBlock);
+            }
+            tiles += static_cast<uint32_t>(nt);
+        }
+        a.ntiles = tiles;
+        for (int t = 0; t < cur_tensors; ++t)
+            std::memcpy(a.blob + t * ptr_block, cur_ptrs[t].data(), ptr_block);
+        std::memcpy(a.blob + a.pieces_offset, cur_pieces.data(), cur_pieces.size() * sizeof(ar::MultiPiece));
+        batches.push_back(a);
+        cur_tensors = 0;
+        cur_pieces.clear();
+        cur_ptrs.clear();
+    };
+    uint64_t off = 0;
+    for (int t = 0; t < ntensors; ++t) {
+        const uint64_t cnt = counts[t];
+        if (cnt == 0) continue;
+        std::vector<ar::MultiPiece> pieces;
+        bool vec = true;
+        std::vector<const void*> ptrs(2 * n);
+        for (int r = 0; r < n; ++r) {
+            ptrs[r] = sendbufs[static_cast<size_t>(t) * n + r];
+            ptrs[n + r] = recvbufs[static_cast<size_t>(t) * n + r];
+            vec = vec && aligned16(ptrs[r]) && aligned16(ptrs[n + r]);
+        }
+        for (uint64_t c = off / q; c * q < off + cnt; ++c) {
+            const uint64_t lo = std::max(off, c * q), hi = std::min(off + cnt, (c + 1) * q);
+            ar::MultiPiece pc{};
+            pc.j0 = lo - off;
+            pc.len = hi - lo;
+            pc.chunk = static_cast<uint8_t>(c);
+            pc.vec = vec ? 1 : 0;
+            pieces.push_back(pc);
+        }
+        const size_t need = (cur_tensors + 1) * ptr_block + (cur_pieces.size() + pieces.size()) * sizeof(ar::MultiPiece);
+        if (need > sizeof(cur.blob)) flush();
+        for (auto& pc : pieces) {
+            pc.tensor = static_cast<uint16_t>(cur_tensors);
+            cur_pieces.push_back(pc);
+        }
+        cur_ptrs.push_back(std::move(ptrs));
+        ++cur_tensors;
+        off += cnt;
+    }
+    flush();
+    if (comm->debug)
+        std::fprintf(stderr, "[allreduce] all_reduce_multi n=%d tensors=%d total=%llu dtype=%s op=%d batches=%zu\n", n,
+                     ntensors, static_cast<unsigned long long>(total), dtype_name(dtype), static_cast<int>(op),
+                     batches.size());
+    const int cap = comm->num_cus * 8;
+    return run_eager(comm, stream, static_cast<int>(batches.size()), [&](hipStream_t s, StepTimer* t) {
+        for (const auto& a : batches) {
+            hipError_t err = ar::launch_multi_reduce(a, dtype, op, static_cast<int>(std::min<uint32_t>(a.ntiles, cap)), s);
+            if (err == hipSuccess) err = tick(t);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    });
+}
+
 AR_EXPORT const char* ar_result_string(ar_result_t result)
 {
     switch (result) {

@@ -75,6 +75,31 @@ hipError_t launch_tree_reduce_level(const TreeArgs& a, ar_dtype_t dtype, ar_op_t
                                     hipStream_t stream);
 hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int grid_x, hipStream_t stream);
 
+// Coalesced multi-tensor all-reduce, one launch per batch of tensors. The
+// blob holds, from offset 0, 2n pointers per tensor (n send then n recv),
+// and from `pieces_offset` the pieces: a piece is the part of one tensor that
+// falls in one ring chunk. Tiles (kBlock vectors, or kBlock elements when the
+// tensor's pointers are not all 16-byte aligned) are numbered across pieces.
+struct MultiPiece {
+    uint64_t j0;     // first element of the piece inside its tensor
+    uint64_t len;    // elements
+    uint32_t tile0;  // first tile of the piece
+    uint16_t tensor; // index of the tensor's pointer block in the blob
+    uint8_t chunk;   // ring chunk (the fold starts at rank `chunk`)
+    uint8_t vec;     // 1: 16-byte vectors in the body, elements at the ends
+};
+static_assert(sizeof(MultiPiece) == 24, "MultiPiece layout");
+constexpr int kMultiBlobBytes = 3840;
+struct MultiArgs {
+    int n;
+    int npieces;
+    uint32_t ntiles;
+    uint32_t pieces_offset;  // bytes into blob
+    alignas(16) unsigned char blob[kMultiBlobBytes];
+};
+
+hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, int grid_x, hipStream_t stream);
+
 // All-to-all block copies: row y copies block p of send[r] to block r of
 // recv[p], `blk` bytes. step < 0: all n*n (r, p) pairs, row y = r*n + p;
 // step s >= 0: the n pairs (r, (r + s) mod n), row y = r.

@@ -216,10 +216,10 @@ __device__ __forceinline__ void chunk_range(uint64_t q, uint64_t count, int c, u
 // ---------------------------------------------------------------------------
 // Element i of chunk c, all ranks, in ring order.
 template <class F, int OP>
-__device__ __forceinline__ typename F::Acc fold_elem(const ReduceArgs& a, int c, int n, uint64_t i)
+__device__ __forceinline__ typename F::Acc fold_elem(const void* const* send, int c, int n, uint64_t i)
 {
-    typename F::Acc acc = F::ld(a.send[c], i);
-    for (int k = 1; k < n; ++k) acc = combine<OP>(F::ld(a.send[wrap_rank(c + k, n)], i), acc);
+    typename F::Acc acc = F::ld(send[c], i);
+    for (int k = 1; k < n; ++k) acc = combine<OP>(F::ld(send[wrap_rank(c + k, n)], i), acc);
     return acc;
 }
 
@@ -227,14 +227,14 @@ __device__ __forceinline__ typename F::Acc fold_elem(const ReduceArgs& a, int c,
 // rank count at compile time (all NR loads issued before the first combine);
 // NR == 0 takes it from the arguments and loads in batches of 8.
 template <class F, int OP, int NR>
-__device__ __forceinline__ void fold_vec(const ReduceArgs& a, int c, int n, uint64_t vi, typename F::Acc* acc)
+__device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, uint64_t vi, typename F::Acc* acc)
 {
     using Acc = typename F::Acc;
     constexpr int E = F::kEpv;
     if constexpr (NR > 0) {
         u32x4 x[NR];
 #pragma unroll
-        for (int k = 0; k < NR; ++k) x[k] = ld16_nt(a.send[wrap_rank(c + k, NR)], vi);
+        for (int k = 0; k < NR; ++k) x[k] = ld16_nt(send[wrap_rank(c + k, NR)], vi);
         F::unpack(x[0], acc);
 #pragma unroll
         for (int k = 1; k < NR; ++k) {
@@ -244,13 +244,13 @@ __device__ __forceinline__ void fold_vec(const ReduceArgs& a, int c, int n, uint
             for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
         }
     } else {
-        F::unpack(ld16_nt(a.send[c], vi), acc);
+        F::unpack(ld16_nt(send[c], vi), acc);
         for (int k = 1; k < n; k += 8) {
             const int b = min(8, n - k);
             u32x4 x[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (j < b) x[j] = ld16_nt(a.send[wrap_rank(c + k + j, n)], vi);
+                if (j < b) x[j] = ld16_nt(send[wrap_rank(c + k + j, n)], vi);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if (j < b) {
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     for (uint64_t v = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; v < nv; v += stride) {
         Acc acc[E];
-        fold_vec<F, OP, NR>(a, c, n, v0 + v, acc);
+        fold_vec<F, OP, NR>(a.send, c, n, v0 + v, acc);
 #pragma unroll
         for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
         const u32x4 out = F::pack(acc);
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     if (blockIdx.x == 0) {
         const uint64_t i = lo + nv * E + threadIdx.x;
         if (i < hi) {
-            const Acc x = finalize<OP>(fold_elem<F, OP>(a, c, n, i), n);
+            const Acc x = finalize<OP>(fold_elem<F, OP>(a.send, c, n, i), n);
             if constexpr (SCATTER) {
                 F::st(a.recv[c], i - lo, x);
             } else {
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_scalar(const ReduceArgs a
     chunk_range(a.q, a.count, c, lo, hi);
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     for (uint64_t i = lo + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < hi; i += stride) {
-        const typename F::Acc x = finalize<OP>(fold_elem<F, OP>(a, c, n, i), n);
+        const typename F::Acc x = finalize<OP>(fold_elem<F, OP>(a.send, c, n, i), n);
         if constexpr (SCATTER) {
             F::st(a.recv[c], i - lo, x);
         } else {
@@ -738,6 +738,75 @@ __global__ __launch_bounds__(kBlock) void tree_bcast_level(const TreeArgs a, uin
 }
 
 // ---------------------------------------------------------------------------
+// coalesced multi-tensor all-reduce: the tensors of each rank form one
+// virtual flat bucket (concatenated in order), chunked as one buffer, so the
+// bits equal a flat-bucket all-reduce, without packing copies
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ const MultiPiece& multi_piece(const MultiArgs& a, uint32_t tile)
+{
+    const MultiPiece* pieces = reinterpret_cast<const MultiPiece*>(a.blob + a.pieces_offset);
+    int lo = 0, hi = a.npieces - 1;  // last piece whose first tile is <= tile
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pieces[mid].tile0 <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    return pieces[lo];
+}
+
+// One workgroup per tile (kBlock vectors, or kBlock elements for scalar
+// pieces); a tile lies inside one piece, so the chunk (ring order) and the
+// tensor (pointers) are uniform across the workgroup.
+template <class F, int OP>
+__global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const int n = a.n;
+    for (uint32_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        const MultiPiece& pc = multi_piece(a, tile);
+        // The blob's pointers are read-only kernel arguments; the recv half
+        // holds device addresses the kernel writes through.
+        const uintptr_t* block = reinterpret_cast<const uintptr_t*>(a.blob) + static_cast<uint64_t>(pc.tensor) * 2 * n;
+        const void* const* send = reinterpret_cast<const void* const*>(block);
+        void* const* recv = reinterpret_cast<void* const*>(const_cast<uintptr_t*>(block + n));
+        const int c = pc.chunk;
+        const uint32_t ti = tile - pc.tile0;
+        const uint64_t j_end = pc.j0 + pc.len;
+        if (pc.vec) {
+            const uint64_t vb = (pc.j0 + E - 1) / E, ve = j_end / E;
+            const uint64_t v = vb + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
+            if (v < ve) {
+                Acc acc[E];
+                fold_vec<F, OP, 0>(send, c, n, v, acc);
+#pragma unroll
+                for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
+                const u32x4 out = F::pack(acc);
+                for (int r = 0; r < n; ++r) st16_nt(recv[r], v, out);
+            }
+            if (ti == 0) {
+                // elements before the first whole vector and after the last
+                const uint64_t head_end = vb * E < j_end ? vb * E : j_end;
+                const uint64_t nhead = head_end - pc.j0;
+                const uint64_t tail_start = ve * E > head_end ? ve * E : head_end;
+                const uint64_t ntail = j_end - tail_start;
+                if (threadIdx.x < nhead + ntail) {
+                    const uint64_t i = threadIdx.x < nhead ? pc.j0 + threadIdx.x : tail_start + (threadIdx.x - nhead);
+                    const Acc x = finalize<OP>(fold_elem<F, OP>(send, c, n, i), n);
+                    for (int r = 0; r < n; ++r) F::st(recv[r], i, x);
+                }
+            }
+        } else {
+            const uint64_t i = pc.j0 + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
+            if (i < j_end) {
+                const Acc x = finalize<OP>(fold_elem<F, OP>(send, c, n, i), n);
+                for (int r = 0; r < n; ++r) F::st(recv[r], i, x);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // all-to-all [handbook "集合通信原语", section 五个原语]: rank r's block p
 // becomes rank p's block r
 // ---------------------------------------------------------------------------
@@ -919,6 +988,35 @@ hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int
     if (vec) hipLaunchKernelGGL((tree_bcast_level<true>), grid, dim3(kBlock), 0, stream, a, bytes);
     else hipLaunchKernelGGL((tree_bcast_level<false>), grid, dim3(kBlock), 0, stream, a, bytes);
     return hipGetLastError();
+}
+
+namespace {
+template <class F>
+hipError_t multi_op(const MultiArgs& a, ar_op_t op, int grid_x, hipStream_t s)
+{
+    const dim3 grid(grid_x), block(kBlock);
+    switch (op) {
+    case AR_SUM: hipLaunchKernelGGL((multi_reduce<F, AR_SUM>), grid, block, 0, s, a); break;
+    case AR_AVG: hipLaunchKernelGGL((multi_reduce<F, AR_AVG>), grid, block, 0, s, a); break;
+    case AR_MAX: hipLaunchKernelGGL((multi_reduce<F, AR_MAX>), grid, block, 0, s, a); break;
+    case AR_MIN: hipLaunchKernelGGL((multi_reduce<F, AR_MIN>), grid, block, 0, s, a); break;
+    case AR_PROD: hipLaunchKernelGGL((multi_reduce<F, AR_PROD>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, int grid_x, hipStream_t stream)
+{
+    switch (dtype) {
+    case AR_FLOAT32: return multi_op<F32>(a, op, grid_x, stream);
+    case AR_FLOAT16: return multi_op<F16>(a, op, grid_x, stream);
+    case AR_BFLOAT16: return multi_op<BF16>(a, op, grid_x, stream);
+    case AR_INT32: return multi_op<I32>(a, op, grid_x, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 namespace {
