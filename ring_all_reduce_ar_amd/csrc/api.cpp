@@ -166,10 +166,15 @@ int grid_for(const ar_comm* comm, uint64_t units_per_row, int rows, int per_cu =
     return static_cast<int>(std::min(want, cap));
 }
 
-// Workgroups per CU for the fused reduction: measured on MI355X (8 ranks,
-// 16-byte vectors), 16 per CU is ~2% faster up to 128 MiB per rank, 8 per CU
-// ~2% faster for multi-GB ranks.
-int fused_per_cu(size_t bytes_per_rank) { return bytes_per_rank <= (size_t(128) << 20) ? 16 : 8; }
+// Workgroups per CU for the fused reduction, as measured on MI355X with
+// 16-byte vectors: at 8 ranks 16 per CU is ~2% faster up to 128 MiB per rank
+// and 8 per CU ~2% faster for multi-GB ranks; at 64 ranks 16 per CU is ~3%
+// faster (256 MiB per rank).
+int fused_per_cu(size_t bytes_per_rank, int nranks)
+{
+    if (nranks >= 32) return 16;
+    return bytes_per_rank <= (size_t(128) << 20) ? 16 : 8;
+}
 
 // Records the start of a call and the end of each step when timing is on.
 struct StepTimer {
@@ -469,7 +474,7 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         a.count = count;
         a.q = count;
         a.n = n;
-        const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, fused_per_cu(count * e));
+        const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, fused_per_cu(count * e, n));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -543,7 +548,7 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         a.count = count;
         a.q = q;
         a.n = n;
-        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes));
+        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, gx, s);
             return err != hipSuccess ? err : tick(t);
