@@ -21,29 +21,63 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liballreduce.so")
-SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "kernels.hip")]
+OBJDIR = os.path.join(PKG, "_build")
+# Two translation units per dtype (ring kernels, tree kernels: the heavy
+# template instantiations), the dtype switch / copy kernels and the C ABI;
+# compiled in parallel, then linked.
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("dtype_f32.hip", "dtype_f16.hip", "dtype_bf16.hip", "dtype_i32.hip", "tree_f32.hip", "tree_f16.hip",
+            "tree_bf16.hip", "tree_i32.hip", "kernels.hip", "api.cpp")]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-command-line-argument",
+         f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def hipcc_command(out: str, extra=()):
-    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
-            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}", *extra,
-            "-o", out, *SOURCES]
+def hipcc_compile(src: str, obj: str):
+    return [HIPCC, *FLAGS, "-c", "-o", obj, src]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into liballreduce.so (always recompiles)."""
+def hipcc_link(objs, out: str):
+    return [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")] + \
+           [os.path.join(INCLUDE, h) for h in os.listdir(INCLUDE)]
+    return max(os.path.getmtime(d) for d in deps) > os.path.getmtime(obj)
+
+
+def build(verbose: bool = False, jobs: int = 0, incremental: bool = False) -> str:
+    """Compile every source into liballreduce.so (always recompiles unless
+    `incremental`, which skips objects newer than their source and headers)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in SOURCES]
+    pending = [(s, o) for s, o in zip(SOURCES, objs) if not incremental or _stale(s, o)]
+    running = []
+    failed = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            src, obj = pending.pop(0)
+            cmd = hipcc_compile(src, obj)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            running.append((src, subprocess.Popen(cmd)))
+        src, proc = running.pop(0)
+        if proc.wait() != 0:
+            failed.append(src)
+    if failed:
+        raise subprocess.CalledProcessError(1, f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    subprocess.run(hipcc_link(objs, tmp), check=True)
     os.replace(tmp, LIB)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -166,6 +166,24 @@ int grid_for(const ar_comm* comm, uint64_t units_per_row, int rows, int per_cu =
     return static_cast<int>(std::min(want, cap));
 }
 
+// The last-level cache of MI355X (Infinity Cache): a fused call whose
+// distinct bytes fit in it uses cached loads/stores, else non-temporal ones.
+constexpr uint64_t kLastLevelCacheBytes = uint64_t(256) << 20;
+
+bool use_nt(uint64_t footprint_bytes) { return footprint_bytes > kLastLevelCacheBytes; }
+
+// Distinct bytes of the rank buffers: in-place ranks count once.
+uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t send_bytes, uint64_t recv_bytes)
+{
+    uint64_t f = 0;
+    for (int r = 0; r < n; ++r) {
+        const uintptr_t s = reinterpret_cast<uintptr_t>(send[r]), d = reinterpret_cast<uintptr_t>(recv[r]);
+        const bool nested = (d >= s && d + recv_bytes <= s + send_bytes) || (s >= d && s + send_bytes <= d + recv_bytes);
+        f += nested ? std::max(send_bytes, recv_bytes) : send_bytes + recv_bytes;
+    }
+    return f;
+}
+
 // Workgroups per CU for the fused reduction, as measured on MI355X with
 // 16-byte vectors: at 8 ranks 16 per CU is ~2% faster up to 128 MiB per rank
 // and 8 per CU ~2% faster for multi-GB ranks; at 64 ranks 16 per CU is ~3%
@@ -475,8 +493,9 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         a.q = count;
         a.n = n;
         const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, fused_per_cu(count * e, n));
+        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, count * e, count * e));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, gx, s);
+            hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -548,9 +567,10 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         a.count = count;
         a.q = q;
         a.n = n;
+        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
         const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, gx, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -636,8 +656,9 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.count = total;
         a.q = q;
         a.n = n;
+        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, sbytes, rbytes));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, gx, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -696,8 +717,9 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
         fill_ptrs(a, n, sendbufs, recvbufs);
         a.total = blk;
         a.n = n;
+        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, blk, rbytes));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_gather(a, vec, gx, s);
+            hipError_t err = ar::launch_fused_gather(a, vec, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -768,11 +790,12 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
     a.blk = blk;
     a.n = n;
     const uint64_t units = vec ? ceil_div(blk, 16) : ceil_div(blk, 2);
+    const bool nt = use_nt(2 * static_cast<uint64_t>(n) * total);
     if (!stepwise) {
         a.step = -1;
         const int gx = grid_for(comm, units, n * n);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_all_to_all(a, vec, gx, s);
+            hipError_t err = ar::launch_all_to_all(a, vec, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -780,7 +803,7 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int st = 0; st < n; ++st) {
             a.step = st;
-            hipError_t err = ar::launch_all_to_all(a, vec, gx, s);
+            hipError_t err = ar::launch_all_to_all(a, vec, nt, gx, s);
             if (err == hipSuccess) err = tick(t);
             if (err != hipSuccess) return err;
         }
@@ -921,9 +944,13 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
                      ntensors, static_cast<unsigned long long>(total), dtype_name(dtype), static_cast<int>(op),
                      batches.size());
     const int cap = comm->num_cus * 8;
+    uint64_t touched = 0;
+    for (const Interval& x : iv) touched += x.hi - x.lo;
+    const bool nt = use_nt(touched);
     return run_eager(comm, stream, static_cast<int>(batches.size()), [&](hipStream_t s, StepTimer* t) {
         for (const auto& a : batches) {
-            hipError_t err = ar::launch_multi_reduce(a, dtype, op, static_cast<int>(std::min<uint32_t>(a.ntiles, cap)), s);
+            hipError_t err =
+                ar::launch_multi_reduce(a, dtype, op, nt, static_cast<int>(std::min<uint32_t>(a.ntiles, cap)), s);
             if (err == hipSuccess) err = tick(t);
             if (err != hipSuccess) return err;
         }

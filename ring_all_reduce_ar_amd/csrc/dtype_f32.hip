@@ -1,0 +1,9 @@
+// dtype_f32.hip -- instantiates the F32 ring kernels (see kernels_impl.h).
+#define AR_INSTANTIATE_RING
+#include "kernels_impl.h"
+
+namespace ar {
+namespace detail {
+AR_RING_INSTANTIATIONS(F32, )
+}  // namespace detail
+}  // namespace ar

@@ -69,7 +69,7 @@ struct TreeArgs {
     int last;  // the root's final level: finalize (AVG, rounding) into recv[0]
 };
 
-hipError_t launch_tree_fused(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
+hipError_t launch_tree_fused(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, int grid_x,
                              hipStream_t stream);
 hipError_t launch_tree_reduce_level(const TreeArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
                                     hipStream_t stream);
@@ -98,7 +98,8 @@ struct MultiArgs {
     alignas(16) unsigned char blob[kMultiBlobBytes];
 };
 
-hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, int grid_x, hipStream_t stream);
+hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, int grid_x,
+                               hipStream_t stream);
 
 // All-to-all block copies: row y copies block p of send[r] to block r of
 // recv[p], `blk` bytes. step < 0: all n*n (r, p) pairs, row y = r*n + p;
@@ -111,15 +112,16 @@ struct A2AArgs {
     int step;
 };
 
-hipError_t launch_all_to_all(const A2AArgs& a, bool vec, int grid_x, hipStream_t stream);
+hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream);
 
 // Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
-// has checked alignment and q % (16/elem) == 0).
-hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec,
+// has checked alignment and q % (16/elem) == 0); `nt` selects non-temporal
+// loads and stores (footprints beyond the last-level cache) over cached ones.
+hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
                                int grid_x, hipStream_t stream);
 
 // Fused all-gather: block p of send[p] (blk bytes) to recv[r] + p*blk for all r.
-hipError_t launch_fused_gather(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);
+hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream);
 
 hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x, hipStream_t stream);
 

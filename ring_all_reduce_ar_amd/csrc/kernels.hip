@@ -1,952 +1,20 @@
-// kernels.hip -- HIP kernels of the ring all-reduce for CDNA4 (gfx950).
-//
-// The reduction is elementwise and HBM-bound: one combine per element and
-// rank against 2*sizeof(T) bytes moved, far below any matrix-core ridge, so
-// there is no MFMA here. What matters is moving bytes: 16-byte (dwordx4)
-// loads and non-temporal stores, one wavefront-uniform chunk per workgroup
-// row so the rank order of the fold is a scalar (SGPR) choice, and enough
-// loads in flight per CU.
-//
-// Ring order [geek-doc "训练梯度同步与集合通信", section 三; handbook
-// "集合通信原语", section 环形 all-reduce 与通信量]: chunk c of the buffer is
-// reduced by the ring as acc = x_c, then acc = x_{c+k} (+) acc for
-// k = 1..n-1 (ranks mod n). Every kernel below folds in exactly that order,
-// so the fused and stepwise modes give the same bits.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "kernels.h"
+// kernels.hip -- the launch functions of kernels.h: the switch over dtypes
+// (whose kernels are instantiated in dtype_*.hip) and the dtype-free copy
+// kernels (all-gather, all-to-all, ring copy steps, tree broadcast).
+#include "kernels_impl.h"
 
 namespace ar {
+using namespace detail;
+
 namespace {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// element formats
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
-__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
-
-__device__ __forceinline__ float half_to_f32(uint32_t h)
-{
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
-}
-
-// v_cvt_f16_f32: round to nearest even (the default mode), subnormals kept.
-__device__ __forceinline__ uint32_t f32_to_half(float f)
-{
-    if (__builtin_isnan(f)) return ((as_u(f) >> 16) & 0x8000u) | 0x7E00u;
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return as_f(b << 16); }
-
-// bfloat16 keeps the top 16 bits of the fp32 pattern; adding 0x7FFF plus the
-// lowest kept bit rounds the dropped 16 bits to nearest, ties to even (a
-// carry into the exponent is the correct rounding up, up to infinity).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
-{
-    uint32_t u = as_u(f);
-    if (__builtin_isnan(f)) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-struct F32 {
-    using Acc = float;
-    static constexpr int kEpv = 4;  // elements per 16-byte vector
-    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return static_cast<const float*>(p)[i]; }
-    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { static_cast<float*>(p)[i] = v; }
-    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
-    {
-        a[0] = as_f(v.x); a[1] = as_f(v.y); a[2] = as_f(v.z); a[3] = as_f(v.w);
-    }
-    static __device__ __forceinline__ u32x4 pack(const Acc* a)
-    {
-        return u32x4{as_u(a[0]), as_u(a[1]), as_u(a[2]), as_u(a[3])};
-    }
-};
-
-struct I32 {
-    using Acc = uint32_t;  // two's-complement wrap
-    static constexpr int kEpv = 4;
-    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return static_cast<const uint32_t*>(p)[i]; }
-    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { static_cast<uint32_t*>(p)[i] = v; }
-    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a) { a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w; }
-    static __device__ __forceinline__ u32x4 pack(const Acc* a) { return u32x4{a[0], a[1], a[2], a[3]}; }
-};
-
-struct F16 {
-    using Acc = float;
-    static constexpr int kEpv = 8;
-    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i)
-    {
-        return half_to_f32(static_cast<const uint16_t*>(p)[i]);
-    }
-    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v)
-    {
-        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_half(v));
-    }
-    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
-    {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            a[2 * j] = half_to_f32(w[j] & 0xFFFFu);
-            a[2 * j + 1] = half_to_f32(w[j] >> 16);
-        }
-    }
-    static __device__ __forceinline__ u32x4 pack(const Acc* a)
-    {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = f32_to_half(a[2 * j]) | (f32_to_half(a[2 * j + 1]) << 16);
-        return u32x4{w[0], w[1], w[2], w[3]};
-    }
-};
-
-struct BF16 {
-    using Acc = float;
-    static constexpr int kEpv = 8;
-    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i)
-    {
-        return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-    }
-    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v)
-    {
-        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
-    }
-    static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
-    {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            a[2 * j] = as_f(w[j] << 16);
-            a[2 * j + 1] = as_f(w[j] & 0xFFFF0000u);
-        }
-    }
-    static __device__ __forceinline__ u32x4 pack(const Acc* a)
-    {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16(a[2 * j]) | (f32_to_bf16(a[2 * j + 1]) << 16);
-        return u32x4{w[0], w[1], w[2], w[3]};
-    }
-};
-
-// ---------------------------------------------------------------------------
-// reduce ops: local (+) incoming [mhpq.cn all-reduce article, section 2.1]
-// ---------------------------------------------------------------------------
-// MAX/MIN: NaN if either operand is NaN; equal operands (including +0/-0)
-// combine their sign bits so that +0 > -0 and the op is commutative.
-__device__ __forceinline__ float fp_max(float a, float b)
-{
-    if (__builtin_isnan(a) || __builtin_isnan(b)) return as_f(0x7FC00000u);
-    if (a == b) return as_f(as_u(a) & as_u(b));
-    return a > b ? a : b;
-}
-
-__device__ __forceinline__ float fp_min(float a, float b)
-{
-    if (__builtin_isnan(a) || __builtin_isnan(b)) return as_f(0x7FC00000u);
-    if (a == b) return as_f(as_u(a) | as_u(b));
-    return a < b ? a : b;
-}
-
-template <int OP>
-__device__ __forceinline__ float combine(float local, float in)
-{
-    if constexpr (OP == AR_SUM || OP == AR_AVG) return local + in;
-    else if constexpr (OP == AR_PROD) return local * in;
-    else if constexpr (OP == AR_MAX) return fp_max(local, in);
-    else return fp_min(local, in);
-}
-
-template <int OP>
-__device__ __forceinline__ uint32_t combine(uint32_t local, uint32_t in)
-{
-    if constexpr (OP == AR_SUM || OP == AR_AVG) return local + in;
-    else if constexpr (OP == AR_PROD) return local * in;
-    else if constexpr (OP == AR_MAX) return static_cast<int32_t>(local) > static_cast<int32_t>(in) ? local : in;
-    else return static_cast<int32_t>(local) < static_cast<int32_t>(in) ? local : in;
-}
-
-// AVG: the finished sum divided once by n (correctly rounded fp32 divide;
-// int32 truncates toward zero).
-template <int OP>
-__device__ __forceinline__ float finalize(float a, int n)
-{
-    if constexpr (OP == AR_AVG) return a / static_cast<float>(n);
-    else return a;
-}
-
-template <int OP>
-__device__ __forceinline__ uint32_t finalize(uint32_t a, int n)
-{
-    if constexpr (OP == AR_AVG) return static_cast<uint32_t>(static_cast<int32_t>(a) / n);
-    else return a;
-}
-
-// ---------------------------------------------------------------------------
-// memory access
-// ---------------------------------------------------------------------------
-// Streaming loads/stores: each input is read once and each output written
-// once, so both bypass cache retention (nt).
-__device__ __forceinline__ u32x4 ld16_nt(const void* base, uint64_t v)
-{
-    return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + v);
-}
-__device__ __forceinline__ void st16_nt(void* base, uint64_t v, u32x4 x)
-{
-    __builtin_nontemporal_store(x, static_cast<u32x4*>(base) + v);
-}
-__device__ __forceinline__ u32x4 ld16(const void* base, uint64_t v) { return static_cast<const u32x4*>(base)[v]; }
-__device__ __forceinline__ void st16(void* base, uint64_t v, u32x4 x) { static_cast<u32x4*>(base)[v] = x; }
-
-__device__ __forceinline__ int wrap_rank(int r, int n) { return r >= n ? r - n : r; }
-
-__device__ __forceinline__ void chunk_range(uint64_t q, uint64_t count, int c, uint64_t& lo, uint64_t& hi)
-{
-    lo = min(static_cast<uint64_t>(c) * q, count);
-    hi = min(lo + q, count);
-}
-
-// ---------------------------------------------------------------------------
-// fused single-pass reduction
-// ---------------------------------------------------------------------------
-// Element i of chunk c, all ranks, in ring order.
-template <class F, int OP>
-__device__ __forceinline__ typename F::Acc fold_elem(const void* const* send, int c, int n, uint64_t i)
-{
-    typename F::Acc acc = F::ld(send[c], i);
-    for (int k = 1; k < n; ++k) acc = combine<OP>(F::ld(send[wrap_rank(c + k, n)], i), acc);
-    return acc;
-}
-
-// Vector vi (16 bytes) of chunk c, all ranks, in ring order. NR > 0 fixes the
-// rank count at compile time (all NR loads issued before the first combine);
-// NR == 0 takes it from the arguments and loads in batches of 8.
-template <class F, int OP, int NR>
-__device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, uint64_t vi, typename F::Acc* acc)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    if constexpr (NR > 0) {
-        u32x4 x[NR];
-#pragma unroll
-        for (int k = 0; k < NR; ++k) x[k] = ld16_nt(send[wrap_rank(c + k, NR)], vi);
-        F::unpack(x[0], acc);
-#pragma unroll
-        for (int k = 1; k < NR; ++k) {
-            Acc t[E];
-            F::unpack(x[k], t);
-#pragma unroll
-            for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
-        }
-    } else {
-        F::unpack(ld16_nt(send[c], vi), acc);
-        for (int k = 1; k < n; k += 8) {
-            const int b = min(8, n - k);
-            u32x4 x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j < b) x[j] = ld16_nt(send[wrap_rank(c + k + j, n)], vi);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < b) {
-                    Acc t[E];
-                    F::unpack(x[j], t);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] = combine<OP>(t[e], acc[e]);
-                }
-            }
-        }
-    }
-}
-
-// grid = (blocks per chunk, n chunks). Workgroup row y handles chunk y, so the
-// ring order (which rank's buffer is loaded k-th) is uniform per workgroup.
-// All-reduce (SCATTER = false) writes the result to every rank; reduce-scatter
-// (SCATTER = true) writes chunk c to recv[c] only. Every input element is read
-// before any output of the same element is written, by the same thread, so
-// send and recv may be the same buffers.
-template <class F, int OP, int NR, bool SCATTER>
-__global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    const int n = NR > 0 ? NR : a.n;
-    const int c = blockIdx.y;
-    uint64_t lo, hi;
-    chunk_range(a.q, a.count, c, lo, hi);
-    const uint64_t nv = (hi - lo) / E;
-    const uint64_t v0 = lo / E;  // exact: the host requires q % E == 0
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t v = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; v < nv; v += stride) {
-        Acc acc[E];
-        fold_vec<F, OP, NR>(a.send, c, n, v0 + v, acc);
-#pragma unroll
-        for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
-        const u32x4 out = F::pack(acc);
-        if constexpr (SCATTER) {
-            st16_nt(a.recv[c], v, out);
-        } else {
-#pragma unroll
-            for (int r = 0; r < n; ++r) st16_nt(a.recv[r], v0 + v, out);
-        }
-    }
-    // A chunk whose length is not a whole number of vectors (only the last
-    // non-empty one) finishes its < E trailing elements here.
-    if (blockIdx.x == 0) {
-        const uint64_t i = lo + nv * E + threadIdx.x;
-        if (i < hi) {
-            const Acc x = finalize<OP>(fold_elem<F, OP>(a.send, c, n, i), n);
-            if constexpr (SCATTER) {
-                F::st(a.recv[c], i - lo, x);
-            } else {
-                for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
-            }
-        }
-    }
-}
-
-// Element-wise variant for buffers that are not 16-byte aligned or chunks that
-// do not start on a vector boundary.
-template <class F, int OP, bool SCATTER>
-__global__ __launch_bounds__(kBlock) void fused_reduce_scalar(const ReduceArgs a)
-{
-    const int n = a.n;
-    const int c = blockIdx.y;
-    uint64_t lo, hi;
-    chunk_range(a.q, a.count, c, lo, hi);
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t i = lo + static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < hi; i += stride) {
-        const typename F::Acc x = finalize<OP>(fold_elem<F, OP>(a.send, c, n, i), n);
-        if constexpr (SCATTER) {
-            F::st(a.recv[c], i - lo, x);
-        } else {
-            for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// fused all-gather: block p of send[p] -> recv[r] + p*blk for every r
-// ---------------------------------------------------------------------------
-template <bool VEC>
-__global__ __launch_bounds__(kBlock) void fused_gather(const CopyArgs a)
-{
-    const int p = blockIdx.y;
-    const uint64_t blk = a.total;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if constexpr (VEC) {
-        const uint64_t nv = blk / 16, o = p * blk / 16;
-        for (uint64_t v = t0; v < nv; v += stride) {
-            const u32x4 x = ld16_nt(a.send[p], v);
-            for (int r = 0; r < a.n; ++r) st16_nt(a.recv[r], o + v, x);
-        }
-    } else {
-        const uint64_t nh = blk / 2, o = p * blk / 2;
-        const uint16_t* src = static_cast<const uint16_t*>(a.send[p]);
-        for (uint64_t h = t0; h < nh; h += stride) {
-            const uint16_t x = src[h];
-            for (int r = 0; r < a.n; ++r) static_cast<uint16_t*>(a.recv[r])[o + h] = x;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// ring-stepwise mode
-// ---------------------------------------------------------------------------
-// Accumulator slots in the workspace are 32-bit patterns. The conversions
-// take their operand by value: bit-casting a vector element in place (w.y)
-// is compiled as a read of the vector's first element.
-__device__ __forceinline__ void from_bits(uint32_t u, float& out) { out = as_f(u); }
-__device__ __forceinline__ void from_bits(uint32_t u, uint32_t& out) { out = u; }
-__device__ __forceinline__ uint32_t to_bits(float v) { return as_u(v); }
-__device__ __forceinline__ uint32_t to_bits(uint32_t v) { return v; }
-
-template <class F>
-__device__ __forceinline__ void ws_load(const void* ws, uint64_t i, typename F::Acc* acc)
-{
-    constexpr int E = F::kEpv;
-#pragma unroll
-    for (int j = 0; j < E / 4; ++j) {
-        const u32x4 w = ld16(ws, i / 4 + j);
-        from_bits(w.x, acc[4 * j + 0]);
-        from_bits(w.y, acc[4 * j + 1]);
-        from_bits(w.z, acc[4 * j + 2]);
-        from_bits(w.w, acc[4 * j + 3]);
-    }
-}
-
-template <class F>
-__device__ __forceinline__ void ws_store(void* ws, uint64_t i, const typename F::Acc* acc)
-{
-    constexpr int E = F::kEpv;
-#pragma unroll
-    for (int j = 0; j < E / 4; ++j) {
-        const u32x4 w{to_bits(acc[4 * j + 0]), to_bits(acc[4 * j + 1]), to_bits(acc[4 * j + 2]),
-                      to_bits(acc[4 * j + 3])};
-        st16(ws, i / 4 + j, w);
-    }
-}
-
-// One element of a reduce-scatter step at rank r (chunk c, left neighbour).
-template <class F, int OP>
-__device__ __forceinline__ void rs_elem(const StepArgs& a, int r, int left, int c, uint64_t lo, uint64_t i)
-{
-    using Acc = typename F::Acc;
-    const Acc local = F::ld(a.send[r], i);
-    Acc in;
-    if (a.first) in = F::ld(a.send[left], i);
-    else if (a.ws) from_bits(static_cast<const uint32_t*>(a.ws)[i], in);
-    else in = F::ld(a.recv[left], i);
-    Acc v = combine<OP>(local, in);
-    if (a.last) {
-        v = finalize<OP>(v, a.n);
-        if (a.scatter) F::st(a.recv[c], i - lo, v);
-        else F::st(a.recv[r], i, v);
-    } else if (a.ws) {
-        static_cast<uint32_t*>(a.ws)[i] = to_bits(v);
-    } else {
-        F::st(a.recv[r], i, v);
-    }
-}
-
-// Reduce-scatter step s [handbook "集合通信原语", section 环形 all-reduce 与通信量]:
-// every rank r combines chunk (r - s - 1) mod n of its own input with the
-// partial arriving from rank r-1. grid = (blocks, n ranks). The chunks a step
-// writes (rank r, chunk c) and reads from the left (rank r-1, chunk c) are
-// disjoint from what rank r-1 writes in the same step (its chunk c-1), so no
-// staging buffer is needed.
-template <class F, int OP, bool VEC>
-__global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    const int n = a.n;
-    const int r = blockIdx.y;
-    const int left = r == 0 ? n - 1 : r - 1;
-    int c = (r - a.s - 1) % n;
-    if (c < 0) c += n;
-    uint64_t lo, hi;
-    chunk_range(a.q, a.count, c, lo, hi);
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    uint64_t done = lo;
-    if constexpr (VEC) {
-        const uint64_t nv = (hi - lo) / E, v0 = lo / E;
-        for (uint64_t v = t0; v < nv; v += stride) {
-            const uint64_t vi = v0 + v;
-            Acc loc[E], in[E];
-            F::unpack(ld16(a.send[r], vi), loc);
-            if (a.first) F::unpack(ld16(a.send[left], vi), in);
-            else if (a.ws) ws_load<F>(a.ws, vi * E, in);
-            else F::unpack(ld16(a.recv[left], vi), in);
-#pragma unroll
-            for (int j = 0; j < E; ++j) loc[j] = combine<OP>(loc[j], in[j]);
-            if (a.last) {
-#pragma unroll
-                for (int j = 0; j < E; ++j) loc[j] = finalize<OP>(loc[j], n);
-                if (a.scatter) st16(a.recv[c], v, F::pack(loc));
-                else st16(a.recv[r], vi, F::pack(loc));
-            } else if (a.ws) {
-                ws_store<F>(a.ws, vi * E, loc);
-            } else {
-                st16(a.recv[r], vi, F::pack(loc));
-            }
-        }
-        done = lo + nv * E;
-        if (blockIdx.x == 0 && done + threadIdx.x < hi) rs_elem<F, OP>(a, r, left, c, lo, done + threadIdx.x);
-    } else {
-        for (uint64_t i = lo + t0; i < hi; i += stride) rs_elem<F, OP>(a, r, left, c, lo, i);
-    }
-}
-
-// Copy step s of a ring: rank r copies chunk (r - s - shift) mod n from rank
-// r-1 (all-gather phase [handbook, section 环形 all-reduce 与通信量]).
-template <bool VEC>
-__global__ __launch_bounds__(kBlock) void copy_step(const CopyArgs a)
-{
-    const int n = a.n;
-    const int r = blockIdx.y;
-    const int left = r == 0 ? n - 1 : r - 1;
-    int c = (r - a.s - a.shift) % n;
-    if (c < 0) c += n;
-    uint64_t lo, hi;
-    chunk_range(a.qb, a.total, c, lo, hi);
-    const char* src = static_cast<const char*>(a.recv[left]);
-    char* dst = static_cast<char*>(a.recv[r]);
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    uint64_t done = lo;
-    if constexpr (VEC) {
-        const uint64_t nv = (hi - lo) / 16, v0 = lo / 16;
-        for (uint64_t v = t0; v < nv; v += stride) st16(dst, v0 + v, ld16(src, v0 + v));
-        done = lo + nv * 16;
-        if (blockIdx.x != 0) return;
-        for (uint64_t b = done + 2 * threadIdx.x; b < hi; b += 2 * kBlock)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    } else {
-        for (uint64_t b = done + 2 * t0; b < hi; b += 2 * stride)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    }
-}
-
-// send[r] -> recv[r] + r*dst_stride, `total` bytes per rank.
-template <bool VEC>
-__global__ __launch_bounds__(kBlock) void local_copy(const CopyArgs a)
-{
-    const int r = blockIdx.y;
-    const char* src = static_cast<const char*>(a.send[r]);
-    char* dst = static_cast<char*>(a.recv[r]) + static_cast<uint64_t>(r) * a.dst_stride;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    uint64_t done = 0;
-    if constexpr (VEC) {
-        const uint64_t nv = a.total / 16;
-        for (uint64_t v = t0; v < nv; v += stride) st16(dst, v, ld16(src, v));
-        done = nv * 16;
-        if (blockIdx.x != 0) return;
-        for (uint64_t b = done + 2 * threadIdx.x; b < a.total; b += 2 * kBlock)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    } else {
-        for (uint64_t b = 2 * t0; b < a.total; b += 2 * stride)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// tree variant [geek-doc "训练梯度同步与集合通信", section 六]: ranks combine
-// in pairs, pair results combine in pairs again, the root ends with the
-// reduction, which goes back down the tree. For element i the fold is the
-// binomial tree over ranks 0..n-1: T(lo, hi) = T(lo, lo+P) (+) T(lo+P, hi),
-// P the largest power of two below hi-lo. One thread evaluates it with a
-// binary counter: slot[b] holds the partial of an aligned block of 2^b ranks;
-// adding rank r carries through the slots whose bit is set in r (the lower
-// ranks' block is the left operand), and the slots left at the end (the set
-// bits of n) fold from the smallest block upward.
-// ---------------------------------------------------------------------------
-constexpr int kTreeSlots = 7;  // 2^6 = AR_MAX_RANKS
-
-template <class F, int OP, int NR>
-__device__ __forceinline__ void tree_fold_vec(const ReduceArgs& a, int n, uint64_t vi, typename F::Acc* out)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    constexpr int RMAX = NR > 0 ? NR : AR_MAX_RANKS;
-    Acc slot[kTreeSlots][E];
-#pragma unroll
-    for (int rb = 0; rb < RMAX; rb += 8) {
-        if (NR > 0 || rb < n) {
-            u32x4 x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (rb + j < RMAX) x[j] = ld16_nt(a.send[min(rb + j, n - 1)], vi);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = rb + j;  // compile-time after unrolling
-                if (r < RMAX && (NR > 0 || r < n)) {
-                    Acc carry[E];
-                    F::unpack(x[j], carry);
-                    int b = 0;
-#pragma unroll
-                    for (; b < kTreeSlots - 1; ++b) {
-                        if (!((r >> b) & 1)) break;
-#pragma unroll
-                        for (int e = 0; e < E; ++e) carry[e] = combine<OP>(slot[b][e], carry[e]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < E; ++e) slot[b][e] = carry[e];
-                }
-            }
-        }
-    }
-    bool have = false;
-#pragma unroll
-    for (int b = 0; b < kTreeSlots; ++b) {
-        if ((n >> b) & 1) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) out[e] = have ? combine<OP>(slot[b][e], out[e]) : slot[b][e];
-            have = true;
-        }
-    }
-}
-
-template <class F, int OP>
-__device__ __forceinline__ typename F::Acc tree_fold_elem(const ReduceArgs& a, int n, uint64_t i)
-{
-    using Acc = typename F::Acc;
-    Acc slot[kTreeSlots];
-#pragma unroll
-    for (int r = 0; r < AR_MAX_RANKS; ++r) {
-        if (r < n) {
-            Acc carry = F::ld(a.send[r], i);
-            int b = 0;
-#pragma unroll
-            for (; b < kTreeSlots - 1; ++b) {
-                if (!((r >> b) & 1)) break;
-                carry = combine<OP>(slot[b], carry);
-            }
-            slot[b] = carry;
-        }
-    }
-    Acc out{};
-    bool have = false;
-#pragma unroll
-    for (int b = 0; b < kTreeSlots; ++b) {
-        if ((n >> b) & 1) {
-            out = have ? combine<OP>(slot[b], out) : slot[b];
-            have = true;
-        }
-    }
-    return out;
-}
-
-// Fused tree all-reduce: 1-D grid-stride over 16-byte vectors of the whole
-// buffer; every element takes the same tree order.
-template <class F, int OP, int NR>
-__global__ __launch_bounds__(kBlock) void tree_fused_vec(const ReduceArgs a)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    const int n = NR > 0 ? NR : a.n;
-    const uint64_t nv = a.count / E;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t v = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; v < nv; v += stride) {
-        Acc acc[E];
-        tree_fold_vec<F, OP, NR>(a, n, v, acc);
-#pragma unroll
-        for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
-        const u32x4 out = F::pack(acc);
-        for (int r = 0; r < n; ++r) st16_nt(a.recv[r], v, out);
-    }
-    if (blockIdx.x == 0) {
-        const uint64_t i = nv * E + threadIdx.x;
-        if (i < a.count) {
-            const Acc x = finalize<OP>(tree_fold_elem<F, OP>(a, n, i), n);
-            for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
-        }
-    }
-}
-
-template <class F, int OP>
-__global__ __launch_bounds__(kBlock) void tree_fused_scalar(const ReduceArgs a)
-{
-    const int n = a.n;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; i < a.count; i += stride) {
-        const typename F::Acc x = finalize<OP>(tree_fold_elem<F, OP>(a, n, i), n);
-        for (int r = 0; r < n; ++r) F::st(a.recv[r], i, x);
-    }
-}
-
-// Partial of rank x in the stepwise tree: recv[x] for fp32/int32 (storage =
-// accumulator), fp32 workspace slot x/2 for fp16/bf16.
-template <class F>
-__device__ __forceinline__ typename F::Acc tree_partial_ld(const TreeArgs& a, int x, uint64_t i)
-{
-    typename F::Acc v;
-    if (a.ws) from_bits(static_cast<const uint32_t*>(a.ws)[static_cast<uint64_t>(x / 2) * a.ws_stride + i], v);
-    else v = F::ld(a.recv[x], i);
-    return v;
-}
-
-template <class F>
-__device__ __forceinline__ void tree_partial_st(const TreeArgs& a, int x, uint64_t i, typename F::Acc v)
-{
-    if (a.ws) static_cast<uint32_t*>(a.ws)[static_cast<uint64_t>(x / 2) * a.ws_stride + i] = to_bits(v);
-    else F::st(a.recv[x], i, v);
-}
-
-template <class F, int OP>
-__device__ __forceinline__ void tree_reduce_elem(const TreeArgs& a, int r, int q, uint64_t i)
-{
-    using Acc = typename F::Acc;
-    // A rank holds a partial once it has received at level 0, i.e. when it
-    // is even and has a right neighbour; r always has, q only if q+1 < n.
-    const Acc local = a.stride == 1 ? F::ld(a.send[r], i) : tree_partial_ld<F>(a, r, i);
-    const Acc in = (a.stride == 1 || q + 1 >= a.n) ? F::ld(a.send[q], i) : tree_partial_ld<F>(a, q, i);
-    Acc v = combine<OP>(local, in);
-    if (a.last) F::st(a.recv[0], i, finalize<OP>(v, a.n));
-    else tree_partial_st<F>(a, r, i, v);
-}
-
-template <class F, int OP, bool VEC>
-__global__ __launch_bounds__(kBlock) void tree_reduce_level(const TreeArgs a)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    const int r = blockIdx.y * 2 * a.stride;
-    const int q = r + a.stride;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if constexpr (VEC) {
-        const uint64_t nv = a.count / E;
-        const bool local_partial = a.stride != 1, in_partial = a.stride != 1 && q + 1 < a.n;
-        for (uint64_t v = t0; v < nv; v += stride) {
-            Acc loc[E], in[E];
-            if (!local_partial) F::unpack(ld16(a.send[r], v), loc);
-            else if (a.ws) ws_load<F>(static_cast<const uint32_t*>(a.ws) + static_cast<uint64_t>(r / 2) * a.ws_stride, v * E, loc);
-            else F::unpack(ld16(a.recv[r], v), loc);
-            if (!in_partial) F::unpack(ld16(a.send[q], v), in);
-            else if (a.ws) ws_load<F>(static_cast<const uint32_t*>(a.ws) + static_cast<uint64_t>(q / 2) * a.ws_stride, v * E, in);
-            else F::unpack(ld16(a.recv[q], v), in);
-#pragma unroll
-            for (int j = 0; j < E; ++j) loc[j] = combine<OP>(loc[j], in[j]);
-            if (a.last) {
-#pragma unroll
-                for (int j = 0; j < E; ++j) loc[j] = finalize<OP>(loc[j], a.n);
-                st16(a.recv[0], v, F::pack(loc));
-            } else if (a.ws) {
-                ws_store<F>(static_cast<uint32_t*>(a.ws) + static_cast<uint64_t>(r / 2) * a.ws_stride, v * E, loc);
-            } else {
-                st16(a.recv[r], v, F::pack(loc));
-            }
-        }
-        if (blockIdx.x == 0 && nv * E + threadIdx.x < a.count) tree_reduce_elem<F, OP>(a, r, q, nv * E + threadIdx.x);
-    } else {
-        for (uint64_t i = t0; i < a.count; i += stride) tree_reduce_elem<F, OP>(a, r, q, i);
-    }
-}
-
-// Broadcast level: recv[q] = recv[r], count*elem bytes.
-template <bool VEC>
-__global__ __launch_bounds__(kBlock) void tree_bcast_level(const TreeArgs a, uint64_t bytes)
-{
-    const int r = blockIdx.y * 2 * a.stride;
-    const int q = r + a.stride;
-    const char* src = static_cast<const char*>(a.recv[r]);
-    char* dst = static_cast<char*>(a.recv[q]);
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    uint64_t done = 0;
-    if constexpr (VEC) {
-        const uint64_t nv = bytes / 16;
-        for (uint64_t v = t0; v < nv; v += stride) st16_nt(dst, v, ld16(src, v));
-        done = nv * 16;
-        if (blockIdx.x != 0) return;
-        for (uint64_t b = done + 2 * threadIdx.x; b < bytes; b += 2 * kBlock)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    } else {
-        for (uint64_t b = 2 * t0; b < bytes; b += 2 * stride)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// coalesced multi-tensor all-reduce: the tensors of each rank form one
-// virtual flat bucket (concatenated in order), chunked as one buffer, so the
-// bits equal a flat-bucket all-reduce, without packing copies
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ const MultiPiece& multi_piece(const MultiArgs& a, uint32_t tile)
-{
-    const MultiPiece* pieces = reinterpret_cast<const MultiPiece*>(a.blob + a.pieces_offset);
-    int lo = 0, hi = a.npieces - 1;  // last piece whose first tile is <= tile
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pieces[mid].tile0 <= tile) lo = mid;
-        else hi = mid - 1;
-    }
-    return pieces[lo];
-}
-
-// One workgroup per tile (kBlock vectors, or kBlock elements for scalar
-// pieces); a tile lies inside one piece, so the chunk (ring order) and the
-// tensor (pointers) are uniform across the workgroup.
-template <class F, int OP>
-__global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    const int n = a.n;
-    for (uint32_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        const MultiPiece& pc = multi_piece(a, tile);
-        // The blob's pointers are read-only kernel arguments; the recv half
-        // holds device addresses the kernel writes through.
-        const uintptr_t* block = reinterpret_cast<const uintptr_t*>(a.blob) + static_cast<uint64_t>(pc.tensor) * 2 * n;
-        const void* const* send = reinterpret_cast<const void* const*>(block);
-        void* const* recv = reinterpret_cast<void* const*>(const_cast<uintptr_t*>(block + n));
-        const int c = pc.chunk;
-        const uint32_t ti = tile - pc.tile0;
-        const uint64_t j_end = pc.j0 + pc.len;
-        if (pc.vec) {
-            const uint64_t vb = (pc.j0 + E - 1) / E, ve = j_end / E;
-            const uint64_t v = vb + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
-            if (v < ve) {
-                Acc acc[E];
-                fold_vec<F, OP, 0>(send, c, n, v, acc);
-#pragma unroll
-                for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
-                const u32x4 out = F::pack(acc);
-                for (int r = 0; r < n; ++r) st16_nt(recv[r], v, out);
-            }
-            if (ti == 0) {
-                // elements before the first whole vector and after the last
-                const uint64_t head_end = vb * E < j_end ? vb * E : j_end;
-                const uint64_t nhead = head_end - pc.j0;
-                const uint64_t tail_start = ve * E > head_end ? ve * E : head_end;
-                const uint64_t ntail = j_end - tail_start;
-                if (threadIdx.x < nhead + ntail) {
-                    const uint64_t i = threadIdx.x < nhead ? pc.j0 + threadIdx.x : tail_start + (threadIdx.x - nhead);
-                    const Acc x = finalize<OP>(fold_elem<F, OP>(send, c, n, i), n);
-                    for (int r = 0; r < n; ++r) F::st(recv[r], i, x);
-                }
-            }
-        } else {
-            const uint64_t i = pc.j0 + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
-            if (i < j_end) {
-                const Acc x = finalize<OP>(fold_elem<F, OP>(send, c, n, i), n);
-                for (int r = 0; r < n; ++r) F::st(recv[r], i, x);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// all-to-all [handbook "集合通信原语", section 五个原语]: rank r's block p
-// becomes rank p's block r
-// ---------------------------------------------------------------------------
-template <bool VEC>
-__global__ __launch_bounds__(kBlock) void a2a_copy(const A2AArgs a)
-{
-    const int y = blockIdx.y;
-    int r, p;
-    if (a.step < 0) {
-        r = y / a.n;
-        p = y - r * a.n;
-    } else {
-        r = y;
-        p = wrap_rank(y + a.step, a.n);
-    }
-    const char* src = static_cast<const char*>(a.send[r]) + static_cast<uint64_t>(p) * a.blk;
-    char* dst = static_cast<char*>(a.recv[p]) + static_cast<uint64_t>(r) * a.blk;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if constexpr (VEC) {
-        const uint64_t nv = a.blk / 16;
-        for (uint64_t v = t0; v < nv; v += stride) st16_nt(dst, v, ld16_nt(src, v));
-    } else {
-        for (uint64_t b = 2 * t0; b < a.blk; b += 2 * stride)
-            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dispatch
-// ---------------------------------------------------------------------------
-template <class F, int OP, bool SC>
-hipError_t fused_n(const ReduceArgs& a, bool vec, dim3 grid, hipStream_t s)
-{
-    const dim3 block(kBlock);
-    if (!vec) {
-        hipLaunchKernelGGL((fused_reduce_scalar<F, OP, SC>), grid, block, 0, s, a);
-        return hipGetLastError();
-    }
-    switch (a.n) {
-    case 2: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 2, SC>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 3, SC>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 4, SC>), grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC>), grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC>), grid, block, 0, s, a); break;
-    }
-    return hipGetLastError();
-}
-
-template <class F, bool SC>
-hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
-{
-    switch (op) {
-    case AR_SUM: return fused_n<F, AR_SUM, SC>(a, vec, grid, s);
-    case AR_AVG: return fused_n<F, AR_AVG, SC>(a, vec, grid, s);
-    case AR_MAX: return fused_n<F, AR_MAX, SC>(a, vec, grid, s);
-    case AR_MIN: return fused_n<F, AR_MIN, SC>(a, vec, grid, s);
-    case AR_PROD: return fused_n<F, AR_PROD, SC>(a, vec, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
-
 template <bool SC>
-hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, dim3 grid, hipStream_t s)
 {
     switch (dtype) {
-    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, grid, s);
-    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, grid, s);
-    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, grid, s);
-    case AR_INT32: return fused_op<I32, SC>(a, op, vec, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <class F, int OP>
-hipError_t rs_vec(const StepArgs& a, bool vec, dim3 grid, hipStream_t s)
-{
-    if (vec) hipLaunchKernelGGL((rs_step<F, OP, true>), grid, dim3(kBlock), 0, s, a);
-    else hipLaunchKernelGGL((rs_step<F, OP, false>), grid, dim3(kBlock), 0, s, a);
-    return hipGetLastError();
-}
-
-template <class F>
-hipError_t rs_op(const StepArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
-{
-    switch (op) {
-    case AR_SUM: return rs_vec<F, AR_SUM>(a, vec, grid, s);
-    case AR_AVG: return rs_vec<F, AR_AVG>(a, vec, grid, s);
-    case AR_MAX: return rs_vec<F, AR_MAX>(a, vec, grid, s);
-    case AR_MIN: return rs_vec<F, AR_MIN>(a, vec, grid, s);
-    case AR_PROD: return rs_vec<F, AR_PROD>(a, vec, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <class F, int OP>
-hipError_t tree_n(const ReduceArgs& a, bool vec, dim3 grid, hipStream_t s)
-{
-    const dim3 block(kBlock);
-    if (!vec) hipLaunchKernelGGL((tree_fused_scalar<F, OP>), grid, block, 0, s, a);
-    else if (a.n == 2) hipLaunchKernelGGL((tree_fused_vec<F, OP, 2>), grid, block, 0, s, a);
-    else if (a.n == 4) hipLaunchKernelGGL((tree_fused_vec<F, OP, 4>), grid, block, 0, s, a);
-    else if (a.n == 8) hipLaunchKernelGGL((tree_fused_vec<F, OP, 8>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((tree_fused_vec<F, OP, 0>), grid, block, 0, s, a);
-    return hipGetLastError();
-}
-
-template <class F>
-hipError_t tree_op(const ReduceArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
-{
-    switch (op) {
-    case AR_SUM: return tree_n<F, AR_SUM>(a, vec, grid, s);
-    case AR_AVG: return tree_n<F, AR_AVG>(a, vec, grid, s);
-    case AR_MAX: return tree_n<F, AR_MAX>(a, vec, grid, s);
-    case AR_MIN: return tree_n<F, AR_MIN>(a, vec, grid, s);
-    case AR_PROD: return tree_n<F, AR_PROD>(a, vec, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <class F, int OP>
-hipError_t tree_level_vec(const TreeArgs& a, bool vec, dim3 grid, hipStream_t s)
-{
-    if (vec) hipLaunchKernelGGL((tree_reduce_level<F, OP, true>), grid, dim3(kBlock), 0, s, a);
-    else hipLaunchKernelGGL((tree_reduce_level<F, OP, false>), grid, dim3(kBlock), 0, s, a);
-    return hipGetLastError();
-}
-
-template <class F>
-hipError_t tree_level_op(const TreeArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
-{
-    switch (op) {
-    case AR_SUM: return tree_level_vec<F, AR_SUM>(a, vec, grid, s);
-    case AR_AVG: return tree_level_vec<F, AR_AVG>(a, vec, grid, s);
-    case AR_MAX: return tree_level_vec<F, AR_MAX>(a, vec, grid, s);
-    case AR_MIN: return tree_level_vec<F, AR_MIN>(a, vec, grid, s);
-    case AR_PROD: return tree_level_vec<F, AR_PROD>(a, vec, grid, s);
+    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, nt, grid, s);
+    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, nt, grid, s);
+    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, nt, grid, s);
+    case AR_INT32: return fused_op<I32, SC>(a, op, vec, nt, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -955,15 +23,15 @@ hipError_t tree_level_op(const TreeArgs& a, ar_op_t op, bool vec, dim3 grid, hip
 
 int tree_pairs(int n, int stride) { return n > stride ? (n - stride - 1) / (2 * stride) + 1 : 0; }
 
-hipError_t launch_tree_fused(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x,
+hipError_t launch_tree_fused(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, int grid_x,
                              hipStream_t stream)
 {
     const dim3 grid(grid_x);
     switch (dtype) {
-    case AR_FLOAT32: return tree_op<F32>(a, op, vec, grid, stream);
-    case AR_FLOAT16: return tree_op<F16>(a, op, vec, grid, stream);
-    case AR_BFLOAT16: return tree_op<BF16>(a, op, vec, grid, stream);
-    case AR_INT32: return tree_op<I32>(a, op, vec, grid, stream);
+    case AR_FLOAT32: return tree_op<F32>(a, op, vec, nt, grid, stream);
+    case AR_FLOAT16: return tree_op<F16>(a, op, vec, nt, grid, stream);
+    case AR_BFLOAT16: return tree_op<BF16>(a, op, vec, nt, grid, stream);
+    case AR_INT32: return tree_op<I32>(a, op, vec, nt, grid, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -990,51 +58,34 @@ hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int
     return hipGetLastError();
 }
 
-namespace {
-template <class F>
-hipError_t multi_op(const MultiArgs& a, ar_op_t op, int grid_x, hipStream_t s)
-{
-    const dim3 grid(grid_x), block(kBlock);
-    switch (op) {
-    case AR_SUM: hipLaunchKernelGGL((multi_reduce<F, AR_SUM>), grid, block, 0, s, a); break;
-    case AR_AVG: hipLaunchKernelGGL((multi_reduce<F, AR_AVG>), grid, block, 0, s, a); break;
-    case AR_MAX: hipLaunchKernelGGL((multi_reduce<F, AR_MAX>), grid, block, 0, s, a); break;
-    case AR_MIN: hipLaunchKernelGGL((multi_reduce<F, AR_MIN>), grid, block, 0, s, a); break;
-    case AR_PROD: hipLaunchKernelGGL((multi_reduce<F, AR_PROD>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
 
-}  // namespace
 
-hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, int grid_x, hipStream_t stream)
+hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, int grid_x,
+                               hipStream_t stream)
 {
     switch (dtype) {
-    case AR_FLOAT32: return multi_op<F32>(a, op, grid_x, stream);
-    case AR_FLOAT16: return multi_op<F16>(a, op, grid_x, stream);
-    case AR_BFLOAT16: return multi_op<BF16>(a, op, grid_x, stream);
-    case AR_INT32: return multi_op<I32>(a, op, grid_x, stream);
+    case AR_FLOAT32: return multi_op<F32>(a, op, nt, grid_x, stream);
+    case AR_FLOAT16: return multi_op<F16>(a, op, nt, grid_x, stream);
+    case AR_BFLOAT16: return multi_op<BF16>(a, op, nt, grid_x, stream);
+    case AR_INT32: return multi_op<I32>(a, op, nt, grid_x, stream);
     }
     return hipErrorInvalidValue;
 }
 
-namespace {
-}  // namespace
-
-hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, int grid_x,
-                               hipStream_t stream)
+hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
+                               int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
-    return scatter ? fused_dtype<true>(a, dtype, op, vec, grid, stream)
-                   : fused_dtype<false>(a, dtype, op, vec, grid, stream);
+    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, grid, stream)
+                   : fused_dtype<false>(a, dtype, op, vec, nt, grid, stream);
 }
 
-hipError_t launch_fused_gather(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream)
+hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
-    if (vec) hipLaunchKernelGGL((fused_gather<true>), grid, dim3(kBlock), 0, stream, a);
-    else hipLaunchKernelGGL((fused_gather<false>), grid, dim3(kBlock), 0, stream, a);
+    if (!vec) hipLaunchKernelGGL((fused_gather<false, true>), grid, dim3(kBlock), 0, stream, a);
+    else if (nt) hipLaunchKernelGGL((fused_gather<true, true>), grid, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((fused_gather<true, false>), grid, dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1058,11 +109,12 @@ hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_all_to_all(const A2AArgs& a, bool vec, int grid_x, hipStream_t stream)
+hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.step < 0 ? a.n * a.n : a.n);
-    if (vec) hipLaunchKernelGGL((a2a_copy<true>), grid, dim3(kBlock), 0, stream, a);
-    else hipLaunchKernelGGL((a2a_copy<false>), grid, dim3(kBlock), 0, stream, a);
+    if (!vec) hipLaunchKernelGGL((a2a_copy<false, true>), grid, dim3(kBlock), 0, stream, a);
+    else if (nt) hipLaunchKernelGGL((a2a_copy<true, true>), grid, dim3(kBlock), 0, stream, a);
+    else hipLaunchKernelGGL((a2a_copy<true, false>), grid, dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,9 @@
+// tree_f16.hip -- instantiates the F16 tree kernels (see kernels_impl.h).
+#define AR_INSTANTIATE_TREE
+#include "kernels_impl.h"
+
+namespace ar {
+namespace detail {
+AR_TREE_INSTANTIATIONS(F16, )
+}  // namespace detail
+}  // namespace ar

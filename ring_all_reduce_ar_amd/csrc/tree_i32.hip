@@ -1,0 +1,9 @@
+// tree_i32.hip -- instantiates the I32 tree kernels (see kernels_impl.h).
+#define AR_INSTANTIATE_TREE
+#include "kernels_impl.h"
+
+namespace ar {
+namespace detail {
+AR_TREE_INSTANTIATIONS(I32, )
+}  // namespace detail
+}  // namespace ar
