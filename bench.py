@@ -37,7 +37,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "all-reduce algbw/busbw GB/s and % HBM peak, N=8 ranks, 64 MiB–14 GB msgs"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "ring_all_reduce_ar_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "ring_all_reduce_ar_amd", "csrc")
 
 # workload name -> (nranks, count, dtype, op, description)
 WORKLOADS = {
@@ -76,8 +76,14 @@ def fit_line(xs, ys):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel source and of the launch code (grid shapes):
+    counters taken on other sources are not reported."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, mode: str):
