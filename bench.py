@@ -51,6 +51,8 @@ WORKLOADS = {
                   "sweep point: 8 virtual ranks x 256 MiB fp32, uniform[-1,1), SUM, in place"),
     "bucket64": (64, 67_108_864, "f32", "max",
                  "bucket64: 64 virtual ranks x 256 MiB fp32 bucket, uniform[-1,1), MAX, in place"),
+    "bucket8": (8, 67_108_864, "f32", "max",
+                "bucket8: 8 virtual ranks x 256 MiB fp32 bucket, uniform[-1,1), MAX, in place"),
 }
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4}
 CPU_WINDOW_LOG2 = 26  # elements per rank in the CPU oracle's window
@@ -214,7 +216,7 @@ def main():
     ap.add_argument("--workload", default="grad7b", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused", choices=["fused", "stepwise", "graph", "tree", "tree_stepwise"])
     ap.add_argument("--multi", action="store_true",
-                    help="bucket64 only: reduce the bucket as its mixed-size tensors with ar_all_reduce_multi")
+                    help="bucket64/bucket8: reduce the bucket as its mixed-size tensors with ar_all_reduce_multi")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line, sweep 1 KiB .. 256 MiB per rank (8 ranks, fp32 SUM) in every "
@@ -245,13 +247,14 @@ def main():
         sweep(args, torch, ar, synthetic)
         return
     n, count, dtype, op, desc = WORKLOADS[args.workload]
-    wl = args.workload if args.workload in synthetic.WORKLOAD_IDS else "sweep"
+    wl = {"bucket8": "bucket64"}.get(args.workload, args.workload)
+    wl = wl if wl in synthetic.WORKLOAD_IDS else "sweep"
     comm = ar.Comm(n, 0)
     stream = torch.cuda.current_stream()
     sizes = None
     if args.multi:
-        if args.workload != "bucket64" or args.mode != "fused":
-            print("bench.py: --multi applies to --workload bucket64 in fused mode", file=sys.stderr)
+        if args.workload not in ("bucket64", "bucket8") or args.mode != "fused":
+            print("bench.py: --multi applies to --workload bucket64 or bucket8 in fused mode", file=sys.stderr)
             sys.exit(2)
         sizes = synthetic.bucket_sizes(count, ESIZE[dtype], 4096, 64 << 20, seed=5)
         desc += f"; as {len(sizes)} tensors per rank through ar_all_reduce_multi"

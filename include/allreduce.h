@@ -38,7 +38,10 @@
  *    thread-local message for the last failure.
  *  - count == 0 (or recvcount/sendcount == 0) is a successful no-op.
  *  - Results are deterministic: the same inputs give the same bits on every
- *    call and in both modes.
+ *    call, and the ring modes (fused, stepwise, graph) give the same bits.
+ *  - A comm holds mutable state (workspace, timing events, graph cache): calls
+ *    on one comm must not run concurrently from several host threads. Calls
+ *    on different comms may.
  */
 #ifndef LIBALLREDUCE_ALLREDUCE_H
 #define LIBALLREDUCE_ALLREDUCE_H

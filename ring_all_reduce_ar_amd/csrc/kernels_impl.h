@@ -40,8 +40,13 @@ __device__ __forceinline__ float half_to_f32(uint32_t h)
 }
 
 // v_cvt_f16_f32: round to nearest even (the default mode), subnormals kept.
+// The value is pinned in a register first: otherwise the compiler may merge
+// the fp32 multiply that produced it with this conversion into one
+// mixed-precision FMA (v_fma_mix*), which rounds once where the fp32 product
+// followed by the conversion rounds twice.
 __device__ __forceinline__ uint32_t f32_to_half(float f)
 {
+    asm("" : "+v"(f));
     if (__builtin_isnan(f)) return ((as_u(f) >> 16) & 0x8000u) | 0x7E00u;
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
@@ -768,29 +773,33 @@ __global__ __launch_bounds__(kBlock) void tree_bcast_level(const TreeArgs a, uin
 // virtual flat bucket (concatenated in order), chunked as one buffer, so the
 // bits equal a flat-bucket all-reduce, without packing copies
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ const MultiPiece& multi_piece(const MultiArgs& a, uint32_t tile)
+__device__ __forceinline__ int multi_find_piece(const MultiPiece* pieces, int npieces, uint32_t tile)
 {
-    const MultiPiece* pieces = reinterpret_cast<const MultiPiece*>(a.blob + a.pieces_offset);
-    int lo = 0, hi = a.npieces - 1;  // last piece whose first tile is <= tile
+    int lo = 0, hi = npieces - 1;  // last piece whose first tile is <= tile
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (pieces[mid].tile0 <= tile) lo = mid;
         else hi = mid - 1;
     }
-    return pieces[lo];
+    return lo;
 }
 
 // One workgroup per tile (kBlock vectors, or kBlock elements for scalar
 // pieces); a tile lies inside one piece, so the chunk (ring order) and the
-// tensor (pointers) are uniform across the workgroup.
-template <class F, int OP, bool NT>
+// tensor (pointers) are uniform across the workgroup. A workgroup's tiles
+// only increase, so after a binary search for its first tile it finds the
+// next piece by scanning forward. NR > 0 fixes the rank count at compile time.
+template <class F, int OP, int NR, bool NT>
 __global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
 {
     using Acc = typename F::Acc;
     constexpr int E = F::kEpv;
-    const int n = a.n;
+    const int n = NR > 0 ? NR : a.n;
+    const MultiPiece* pieces = reinterpret_cast<const MultiPiece*>(a.blob + a.pieces_offset);
+    int pidx = blockIdx.x < a.ntiles ? multi_find_piece(pieces, a.npieces, blockIdx.x) : 0;
     for (uint32_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        const MultiPiece& pc = multi_piece(a, tile);
+        while (pidx + 1 < a.npieces && pieces[pidx + 1].tile0 <= tile) ++pidx;
+        const MultiPiece& pc = pieces[pidx];
         // The blob's pointers are read-only kernel arguments; the recv half
         // holds device addresses the kernel writes through.
         const uintptr_t* block = reinterpret_cast<const uintptr_t*>(a.blob) + static_cast<uint64_t>(pc.tensor) * 2 * n;
@@ -804,10 +813,11 @@ __global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
             const uint64_t v = vb + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
             if (v < ve) {
                 Acc acc[E];
-                fold_vec<F, OP, 0, NT>(send, c, n, v, acc);
+                fold_vec<F, OP, NR, NT>(send, c, n, v, acc);
 #pragma unroll
                 for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
                 const u32x4 out = F::pack(acc);
+#pragma unroll
                 for (int r = 0; r < n; ++r) stv<NT>(recv[r], v, out);
             }
             if (ti == 0) {
@@ -978,19 +988,26 @@ hipError_t tree_level_op(const TreeArgs& a, ar_op_t op, bool vec, dim3 grid, hip
     return hipErrorInvalidValue;
 }
 
+template <class F, int OP, bool NT>
+hipError_t multi_nr(const MultiArgs& a, int grid_x, hipStream_t s)
+{
+    const dim3 grid(grid_x), block(kBlock);
+    if (a.n == 8) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
 template <class F, bool NT>
 hipError_t multi_nt(const MultiArgs& a, ar_op_t op, int grid_x, hipStream_t s)
 {
-    const dim3 grid(grid_x), block(kBlock);
     switch (op) {
-    case AR_SUM: hipLaunchKernelGGL((multi_reduce<F, AR_SUM, NT>), grid, block, 0, s, a); break;
-    case AR_AVG: hipLaunchKernelGGL((multi_reduce<F, AR_AVG, NT>), grid, block, 0, s, a); break;
-    case AR_MAX: hipLaunchKernelGGL((multi_reduce<F, AR_MAX, NT>), grid, block, 0, s, a); break;
-    case AR_MIN: hipLaunchKernelGGL((multi_reduce<F, AR_MIN, NT>), grid, block, 0, s, a); break;
-    case AR_PROD: hipLaunchKernelGGL((multi_reduce<F, AR_PROD, NT>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case AR_SUM: return multi_nr<F, AR_SUM, NT>(a, grid_x, s);
+    case AR_AVG: return multi_nr<F, AR_AVG, NT>(a, grid_x, s);
+    case AR_MAX: return multi_nr<F, AR_MAX, NT>(a, grid_x, s);
+    case AR_MIN: return multi_nr<F, AR_MIN, NT>(a, grid_x, s);
+    case AR_PROD: return multi_nr<F, AR_PROD, NT>(a, grid_x, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 template <class F>

@@ -329,6 +329,34 @@ def pin_prod_bound(o):
             assert abs(Fraction(float(y[i])) - p) <= Fraction(g) * abs(p), (n, i)
 
 
+def pin_prod_double_rounding(o):
+    """fp16 PROD is an fp32 product in ring order, rounded to fp16 once at the
+    end (mhpq.cn article, section 5.3): on inputs where the last fp32 multiply
+    lands on an fp16 tie, the result is numpy's fp32 product converted by
+    numpy, which differs from rounding the exact product."""
+    import rounding_cases
+    for n in (3, 8):
+        count = n * 64 + 5
+        xs, idx = rounding_cases.ring_prod_inputs(n, count, 7, seed=5 + n)
+        q = -(-count // n)
+        c = np.arange(count) // q
+        order = [(c + k) % n for k in range(n)]
+        x = np.stack(xs)
+        p = x[order[0], np.arange(count)].astype(np.float32)
+        for k in range(1, n - 1):
+            p = p * x[order[k], np.arange(count)].astype(np.float32)
+        last = x[order[n - 1], np.arange(count)]
+        exp = (p * last.astype(np.float32)).astype(np.float16)
+        once = (p.astype(np.float64) * last.astype(np.float64)).astype(np.float16)
+        assert idx.size > 0 and np.all(exp[idx] != once[idx]), "inputs do not separate one rounding from two"
+        folded = o.fold_all_reduce(xs, "f16", "prod")
+        ring = [a.copy() for a in xs]
+        o.ring_all_reduce(ring, "f16", "prod")
+        for r in range(n):
+            assert same_bits(folded[r], exp), (n, r)
+            assert same_bits(ring[r], exp), (n, r)
+
+
 def pin_f16_conversions(o):
     """fp16 <-> fp32 conversions equal numpy's on all 2^16 patterns and on
     random fp32, on every halfway point between adjacent fp16 values and on its
@@ -495,7 +523,8 @@ def pin_tree(o):
 ALL_PINS = [
     pin_worked_example, pin_bytes_sent_page, pin_bytes_closed_form, pin_partition_torch_chunk,
     pin_ring_order, pin_fp32_accumulate, pin_forms_agree, pin_int_brute_force, pin_fp_maxmin,
-    pin_sum_error_bound, pin_avg_pow2, pin_prod_bound, pin_f16_conversions, pin_bf16_conversions,
+    pin_sum_error_bound, pin_avg_pow2, pin_prod_bound, pin_prod_double_rounding, pin_f16_conversions,
+    pin_bf16_conversions,
     pin_rs_ag_equals_ar, pin_all_gather_concat, pin_elements_match, pin_all_to_all,
     pin_tree,
 ]

@@ -116,3 +116,32 @@ def test_caller_capture_replays(mode):
                 gu.assert_same(gu.host(eager[r].view), got[r], dtype, f"eager vs replay {trial} rank {r}")
         ar.ar_comm_set_workspace(comm, None)
         del ws
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i32"])
+@pytest.mark.parametrize("n", [2, 5, 8])
+def test_graph_mode_reduce_scatter_and_all_gather(n, dtype):
+    """The graph-replayed ring for the reduce-scatter and all-gather exports:
+    the first call captures, the later ones (same pointers, new contents)
+    replay; each against the oracle."""
+    with ar.Comm(n, 0) as comm:
+        rc = 1024 + gu.EPV[dtype]
+        send = [gu.RankBuf(n * rc, dtype) for _ in range(n)]
+        recv = [gu.RankBuf(rc, dtype) for _ in range(n)]
+        gathered = [gu.RankBuf(n * rc, dtype) for _ in range(n)]
+        ws = gu.attach_workspace(comm, ar.AR_COLL_REDUCE_SCATTER, n, rc, dtype, "graph")
+        for trial in range(3):
+            xs = gu.make_inputs(n, n * rc, dtype, "avg", seed=trial)
+            for b, x in zip(send, xs):
+                b.view.copy_(x)
+            ar.ar_reduce_scatter(comm, [b.ptr() for b in send], [b.ptr() for b in recv], rc, dtype, "avg", "graph")
+            ar.ar_all_gather(comm, [b.ptr() for b in recv], [b.ptr() for b in gathered], rc, dtype, "graph")
+            torch.cuda.synchronize()
+            exp = oracle.reduce_scatter([gu.host(x) for x in xs], dtype, "avg")
+            exp_ag = oracle.all_gather(exp, dtype)
+            for r in range(n):
+                assert recv[r].guards_ok() and gathered[r].guards_ok()
+                gu.assert_same(gu.host(recv[r].view), exp[r], dtype, f"graph RS n={n} trial {trial} rank {r}")
+                gu.assert_same(gu.host(gathered[r].view), exp_ag[r], dtype, f"graph AG n={n} trial {trial} rank {r}")
+        ar.ar_comm_set_workspace(comm, None)
+        del ws
