@@ -37,6 +37,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "all-reduce algbw/busbw GB/s and % HBM peak, N=8 ranks, 64 MiB–14 GB msgs"
 HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 << 20      # MI355X last-level (Infinity) cache
+ROTATE_BYTES = 1 << 30    # rotated footprint for calls that fit in it
 CSRC = os.path.join(ROOT, "ring_all_reduce_ar_amd", "csrc")
 
 # workload name -> (nranks, count, dtype, op, description)
@@ -259,53 +261,70 @@ def main():
         sizes = synthetic.bucket_sizes(count, ESIZE[dtype], 4096, 64 << 20, seed=5)
         desc += f"; as {len(sizes)} tensors per rank through ar_all_reduce_multi"
 
-    def timed_pass():
-        """Allocate and fill the rank buffers, warm up, time exactly K steps."""
-        print(f"[bench] generating {desc}", file=sys.stderr, flush=True)
-        bufs = synthetic.rank_inputs(wl, n, count, dtype, device="cuda", op=op)
+    s_bytes = count * ESIZE[dtype]
+    # A call whose rank buffers fit in the last-level cache would be timed
+    # warm if it ran on one buffer set back to back; rotate K sets so that
+    # K*N*S >= 1 GiB and every call reads from HBM. The warm figure on one
+    # set is reported beside it, labelled.
+    sets = 1 if n * s_bytes > LLC_BYTES else -(-ROTATE_BYTES // (n * s_bytes))
+
+    def timed_pass(measure_warm: bool):
+        """Allocate and fill the rank buffers, warm up, time exactly K steps
+        (an event after each step gives the per-step times)."""
+        print(f"[bench] generating {desc}" + (f" ({sets} rotating buffer sets)" if sets > 1 else ""),
+              file=sys.stderr, flush=True)
+        bufsets = [synthetic.rank_inputs(wl, n, count, dtype, device="cuda", op=op, salt=k) for k in range(sets)]
         ws = None
         need = ar.ar_workspace_bytes(ar.AR_COLL_ALL_REDUCE, n, count, dtype, args.mode)
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
             ar.ar_comm_set_workspace(comm, ws)
-        ptrs = [b.data_ptr() for b in bufs]
+        ptrsets = [[b.data_ptr() for b in bufs] for bufs in bufsets]
         if sizes is None:
-            def step():
-                ar.ar_all_reduce(comm, ptrs, ptrs, count, dtype, op, args.mode, stream)
+            def step(i):
+                p = ptrsets[i % sets]
+                ar.ar_all_reduce(comm, p, p, count, dtype, op, args.mode, stream)
         else:
             offs = [0]
             for c in sizes[:-1]:
                 offs.append(offs[-1] + c)
-            rows = [[p + o * ESIZE[dtype] for p in ptrs] for o in offs]
+            rowsets = [[[p + o * ESIZE[dtype] for p in ptrs] for o in offs] for ptrs in ptrsets]
 
-            def step():
+            def step(i):
+                rows = rowsets[i % sets]
                 ar.ar_all_reduce_multi(comm, rows, rows, sizes, dtype, op, "fused", stream)
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(args.steps):
-            step()
-        stop.record(stream)
-        torch.cuda.synchronize()
-        ms_ = start.elapsed_time(stop) / args.steps
+
+        def run(k, rotate):
+            for i in range(args.warmup):
+                step(i if rotate else 0)
+            torch.cuda.synchronize()
+            events = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+            torch.cuda.synchronize()
+            events[0].record(stream)
+            for i in range(k):
+                step(i if rotate else 0)
+                events[i + 1].record(stream)
+            torch.cuda.synchronize()
+            per_step = [events[i].elapsed_time(events[i + 1]) for i in range(k)]
+            return events[0].elapsed_time(events[k]) / k, per_step
+
+        print(f"[bench] timing {args.warmup} warmup + {args.steps} steps", file=sys.stderr, flush=True)
+        ms_, per_step = run(args.steps, True)
+        warm = run(args.steps, False)[0] if measure_warm and sets > 1 else None
         ar.ar_comm_set_workspace(comm, None)
-        del bufs, ws
+        del bufsets, ptrsets, ws
         torch.cuda.empty_cache()
-        return ms_
+        return ms_, per_step, warm
 
     # The first allocation of the rank buffers in a fresh process measured up
     # to ~9% slower on MI355X than the same buffers allocated again after a
     # free (same virtual addresses, different physical backing). Both passes
     # are timed; the second is the steady state a long-running job sees and
     # is the reported value; the first is reported beside it.
-    first_ms = timed_pass()
-    ms = timed_pass()
+    first_ms, _, _ = timed_pass(False)
+    ms, per_step, warm_ms = timed_pass(True)
+    per_step.sort()
 
-    s_bytes = count * ESIZE[dtype]
     algbw = s_bytes / (ms * 1e-3) / 1e9
     busbw = algbw * 2 * (n - 1) / n
     # fused: one launch per step; stepwise: 2(N-1) launches, reported against
@@ -322,6 +341,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "first_allocation_ms_per_step": round(first_ms, 4),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                    "max": round(per_step[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -337,6 +358,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
     }
+    if sets > 1:
+        result["config"]["rotating_buffer_sets"] = sets
+        result["cache_resident"] = {"ms_per_step": round(warm_ms, 4),
+                                    "effective_gbps": round(alg_bytes / (warm_ms * 1e-3) / 1e9, 1),
+                                    "note": "one buffer set called back to back; served from the last-level cache"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload)

@@ -148,23 +148,13 @@ struct BF16 {
 // ---------------------------------------------------------------------------
 // reduce ops: local (+) incoming [mhpq.cn all-reduce article, section 2.1]
 // ---------------------------------------------------------------------------
-// MAX/MIN: NaN if either operand is NaN; equal operands (including +0/-0)
-// combine their sign bits so that +0 > -0 and the op is commutative.
-// Written with selects (no early returns): the same result, and no branch
-// blow-up when a fold over many ranks is fully unrolled.
-__device__ __forceinline__ float fp_max(float a, float b)
-{
-    const float bigger = a > b ? a : b;
-    const float r = a == b ? as_f(as_u(a) & as_u(b)) : bigger;
-    return (a != a || b != b) ? as_f(0x7FC00000u) : r;
-}
+// MAX/MIN: NaN if either operand is NaN, and +0 > -0, so both are
+// commutative and associative. That is IEEE 754-2019 maximum/minimum, which
+// gfx950 executes in one instruction (v_maximum3_f32 / v_minimum3_f32).
+// A NaN result may carry an input's payload; only its NaN-ness is specified.
+__device__ __forceinline__ float fp_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-__device__ __forceinline__ float fp_min(float a, float b)
-{
-    const float smaller = a < b ? a : b;
-    const float r = a == b ? as_f(as_u(a) | as_u(b)) : smaller;
-    return (a != a || b != b) ? as_f(0x7FC00000u) : r;
-}
+__device__ __forceinline__ float fp_min(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
 template <int OP>
 __device__ __forceinline__ float combine(float local, float in)
