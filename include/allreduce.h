@@ -209,8 +209,11 @@ ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[], void* co
  * exactly the bits ar_all_reduce gives on the packed bucket. Each tensor may
  * be in place (send == recv); any other overlap is INVALID_ARGUMENT.
  * AR_MODE_FUSED only (other modes: UNSUPPORTED). Launches: one per batch of
- * tensors whose rank pointers fit the kernel arguments (about 3.8 KB: e.g.
- * 24 tensors per launch at 8 ranks, 3 at 64). No workspace. */
+ * tensors whose rank pointers fit the kernel arguments (about 3.8 KB; a
+ * tensor in place on every rank takes n pointers, otherwise 2n: e.g. about
+ * 40 in-place tensors per launch at 8 ranks, 6 at 64). Tensors whose rank
+ * pointers all sit at the same offset from a 16-byte boundary are read and
+ * written in 16-byte vectors; others element by element. No workspace. */
 ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const void* const sendbufs[], void* const recvbufs[],
                                 const size_t counts[], ar_dtype_t dtype, ar_op_t op, ar_mode_t mode,
                                 hipStream_t stream);

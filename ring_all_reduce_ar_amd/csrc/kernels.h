@@ -75,26 +75,48 @@ hipError_t launch_tree_reduce_level(const TreeArgs& a, ar_dtype_t dtype, ar_op_t
                                     hipStream_t stream);
 hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int grid_x, hipStream_t stream);
 
-// Coalesced multi-tensor all-reduce, one launch per batch of tensors. The
-// blob holds, from offset 0, 2n pointers per tensor (n send then n recv),
-// and from `pieces_offset` the pieces: a piece is the part of one tensor that
-// falls in one ring chunk. Tiles (kBlock vectors, or kBlock elements when the
-// tensor's pointers are not all 16-byte aligned) are numbered across pieces.
+// Coalesced multi-tensor all-reduce. The table holds, from offset 0, each
+// tensor's rank pointers (n send then n recv, or just n when every rank's
+// tensor is in place), and from `pieces_offset` the pieces: a piece is the
+// part of one tensor that falls in one ring chunk. Tiles (kBlock vectors, or
+// kBlock elements when the tensor's pointers are not all 16-byte aligned)
+// are numbered across pieces.
+constexpr uint8_t kPieceVec = 1;      // 16-byte vectors in the body, elements at the ends
+constexpr uint8_t kPieceInPlace = 2;  // recv pointers are the send pointers
+constexpr int kPieceShiftBit = 2;     // bits 2..4: a0, the tensor's first 16-byte aligned element
+
+// The 16-byte vectors of a piece [j0, j_end) of a tensor whose element a0 is
+// the first one on a 16-byte boundary (the same a0 for every rank's
+// pointers): vector k holds elements [a0 + kE, a0 + (k+1)E), and the piece's
+// whole vectors are [vb, ve). Shared by the planner and the kernel, which
+// must agree on the tile count.
+__host__ __device__ inline void piece_vectors(uint64_t j0, uint64_t j_end, uint64_t a0, uint64_t E, uint64_t* vb,
+                                              uint64_t* ve)
+{
+    *vb = j0 <= a0 ? 0 : (j0 - a0 + E - 1) / E;
+    *ve = j_end <= a0 ? 0 : (j_end - a0) / E;
+    if (*ve < *vb) *ve = *vb;
+}
 struct MultiPiece {
     uint64_t j0;     // first element of the piece inside its tensor
     uint64_t len;    // elements
     uint32_t tile0;  // first tile of the piece
-    uint16_t tensor; // index of the tensor's pointer block in the blob
+    uint16_t ptrs;   // index of the tensor's first pointer in the table
     uint8_t chunk;   // ring chunk (the fold starts at rank `chunk`)
-    uint8_t vec;     // 1: 16-byte vectors in the body, elements at the ends
+    uint8_t flags;   // kPieceVec | kPieceInPlace | a0 << kPieceShiftBit
 };
 static_assert(sizeof(MultiPiece) == 24, "MultiPiece layout");
 constexpr int kMultiBlobBytes = 3840;
-struct MultiArgs {
+struct MultiHeader {
     int n;
     int npieces;
     uint32_t ntiles;
-    uint32_t pieces_offset;  // bytes into blob
+    uint32_t pieces_offset;  // bytes into the table
+};
+// The table travels in the kernel arguments: one launch per batch of
+// tensors whose pointer blocks and pieces fit.
+struct MultiArgs {
+    MultiHeader h;
     alignas(16) unsigned char blob[kMultiBlobBytes];
 };
 

@@ -28,6 +28,20 @@ namespace detail {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Rank buffers are global memory. Pointers that come from kernel arguments
+// are known to be global; pointers read from a device-memory table are not,
+// and would be accessed with flat instructions. gptr states it.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gptr(const void* p)
+{
+    return (const __attribute__((address_space(1))) T*)(p);
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gptr(void* p)
+{
+    return (__attribute__((address_space(1))) T*)(p);
+}
+
 // ---------------------------------------------------------------------------
 // element formats
 // ---------------------------------------------------------------------------
@@ -66,8 +80,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 struct F32 {
     using Acc = float;
     static constexpr int kEpv = 4;  // elements per 16-byte vector
-    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return static_cast<const float*>(p)[i]; }
-    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { static_cast<float*>(p)[i] = v; }
+    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return gptr<float>(p)[i]; }
+    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { gptr<float>(p)[i] = v; }
     static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
     {
         a[0] = as_f(v.x); a[1] = as_f(v.y); a[2] = as_f(v.z); a[3] = as_f(v.w);
@@ -81,8 +95,8 @@ struct F32 {
 struct I32 {
     using Acc = uint32_t;  // two's-complement wrap
     static constexpr int kEpv = 4;
-    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return static_cast<const uint32_t*>(p)[i]; }
-    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { static_cast<uint32_t*>(p)[i] = v; }
+    static __device__ __forceinline__ Acc ld(const void* p, uint64_t i) { return gptr<uint32_t>(p)[i]; }
+    static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v) { gptr<uint32_t>(p)[i] = v; }
     static __device__ __forceinline__ void unpack(u32x4 v, Acc* a) { a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w; }
     static __device__ __forceinline__ u32x4 pack(const Acc* a) { return u32x4{a[0], a[1], a[2], a[3]}; }
 };
@@ -92,11 +106,11 @@ struct F16 {
     static constexpr int kEpv = 8;
     static __device__ __forceinline__ Acc ld(const void* p, uint64_t i)
     {
-        return half_to_f32(static_cast<const uint16_t*>(p)[i]);
+        return half_to_f32(gptr<uint16_t>(p)[i]);
     }
     static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v)
     {
-        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_half(v));
+        gptr<uint16_t>(p)[i] = static_cast<uint16_t>(f32_to_half(v));
     }
     static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
     {
@@ -121,11 +135,11 @@ struct BF16 {
     static constexpr int kEpv = 8;
     static __device__ __forceinline__ Acc ld(const void* p, uint64_t i)
     {
-        return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+        return bf16_to_f32(gptr<uint16_t>(p)[i]);
     }
     static __device__ __forceinline__ void st(void* p, uint64_t i, Acc v)
     {
-        static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
+        gptr<uint16_t>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
     }
     static __device__ __forceinline__ void unpack(u32x4 v, Acc* a)
     {
@@ -197,14 +211,14 @@ __device__ __forceinline__ uint32_t finalize(uint32_t a, int n)
 // once, so both bypass cache retention (nt).
 __device__ __forceinline__ u32x4 ld16_nt(const void* base, uint64_t v)
 {
-    return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + v);
+    return __builtin_nontemporal_load(gptr<u32x4>(base) + v);
 }
 __device__ __forceinline__ void st16_nt(void* base, uint64_t v, u32x4 x)
 {
-    __builtin_nontemporal_store(x, static_cast<u32x4*>(base) + v);
+    __builtin_nontemporal_store(x, gptr<u32x4>(base) + v);
 }
-__device__ __forceinline__ u32x4 ld16(const void* base, uint64_t v) { return static_cast<const u32x4*>(base)[v]; }
-__device__ __forceinline__ void st16(void* base, uint64_t v, u32x4 x) { static_cast<u32x4*>(base)[v] = x; }
+__device__ __forceinline__ u32x4 ld16(const void* base, uint64_t v) { return gptr<u32x4>(base)[v]; }
+__device__ __forceinline__ void st16(void* base, uint64_t v, u32x4 x) { gptr<u32x4>(base)[v] = x; }
 
 // The fused kernels pick the access flavour per call: when everything the
 // call touches fits in the last-level cache (the 256 MB Infinity Cache of
@@ -217,11 +231,23 @@ __device__ __forceinline__ u32x4 ldv(const void* base, uint64_t v)
     if constexpr (NT) return ld16_nt(base, v);
     else return ld16(base, v);
 }
+// The same at a byte offset (a multiple of 16 past a 16-byte boundary).
+template <bool NT>
+__device__ __forceinline__ u32x4 ldv_at(const void* base, uint64_t byte_off)
+{
+    return ldv<NT>(static_cast<const char*>(base) + byte_off, 0);
+}
+
 template <bool NT>
 __device__ __forceinline__ void stv(void* base, uint64_t v, u32x4 x)
 {
     if constexpr (NT) st16_nt(base, v, x);
     else st16(base, v, x);
+}
+template <bool NT>
+__device__ __forceinline__ void stv_at(void* base, uint64_t byte_off, u32x4 x)
+{
+    stv<NT>(static_cast<char*>(base) + byte_off, 0, x);
 }
 
 __device__ __forceinline__ int wrap_rank(int r, int n) { return r >= n ? r - n : r; }
@@ -247,31 +273,50 @@ __device__ __forceinline__ typename F::Acc fold_elem(const void* const* send, in
 // Vector vi (16 bytes) of chunk c, all ranks, in ring order. NR > 0 fixes the
 // rank count at compile time (all NR loads issued before the first combine);
 // NR == 0 takes it from the arguments and loads in batches of 8.
+// The 16 bytes at byte offset `off` of NR buffers already listed in fold
+// order (the chunk's first rank first): all NR loads are issued, then
+// combined in that order.
 template <class F, int OP, int NR, bool NT>
-__device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, uint64_t vi, typename F::Acc* acc)
+__device__ __forceinline__ void fold_vec_ordered(const void* const (&sp)[NR], uint64_t off, typename F::Acc* acc)
 {
     using Acc = typename F::Acc;
     constexpr int E = F::kEpv;
+    u32x4 x[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) x[k] = ldv_at<NT>(sp[k], off);
+    F::unpack(x[0], acc);
+#pragma unroll
+    for (int k = 1; k < NR; ++k) {
+        Acc t[E];
+        F::unpack(x[k], t);
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
+    }
+}
+
+// Vector vi of every rank, `boff` bytes past the rank pointers (0 unless the
+// vectors start past an unaligned base); the offset is one per-thread value,
+// so the rank pointers stay plain bases.
+template <class F, int OP, int NR, bool NT>
+__device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, uint64_t vi, typename F::Acc* acc,
+                                         uint64_t boff = 0)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const uint64_t off = vi * 16 + boff;
     if constexpr (NR > 0) {
-        u32x4 x[NR];
+        const void* sp[NR];
 #pragma unroll
-        for (int k = 0; k < NR; ++k) x[k] = ldv<NT>(send[wrap_rank(c + k, NR)], vi);
-        F::unpack(x[0], acc);
-#pragma unroll
-        for (int k = 1; k < NR; ++k) {
-            Acc t[E];
-            F::unpack(x[k], t);
-#pragma unroll
-            for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
-        }
+        for (int k = 0; k < NR; ++k) sp[k] = send[wrap_rank(c + k, NR)];
+        fold_vec_ordered<F, OP, NR, NT>(sp, off, acc);
     } else {
-        F::unpack(ldv<NT>(send[c], vi), acc);
+        F::unpack(ldv_at<NT>(send[c], off), acc);
         for (int k = 1; k < n; k += 8) {
             const int b = min(8, n - k);
             u32x4 x[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (j < b) x[j] = ldv<NT>(send[wrap_rank(c + k + j, n)], vi);
+                if (j < b) x[j] = ldv_at<NT>(send[wrap_rank(c + k + j, n)], off);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if (j < b) {
@@ -763,7 +808,25 @@ __global__ __launch_bounds__(kBlock) void tree_bcast_level(const TreeArgs a, uin
 // virtual flat bucket (concatenated in order), chunked as one buffer, so the
 // bits equal a flat-bucket all-reduce, without packing copies
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int multi_find_piece(const MultiPiece* pieces, int npieces, uint32_t tile)
+// The table (pointer blocks and pieces, in the kernel arguments) does not
+// change while a kernel runs: it is read through the constant address space.
+typedef __attribute__((address_space(4))) const unsigned char cbyte;
+typedef __attribute__((address_space(4))) const MultiPiece cpiece;
+typedef __attribute__((address_space(4))) const uintptr_t cuptr;
+
+__device__ __forceinline__ MultiPiece load_piece(cpiece* p)
+{
+    MultiPiece r;
+    r.j0 = p->j0;
+    r.len = p->len;
+    r.tile0 = p->tile0;
+    r.ptrs = p->ptrs;
+    r.chunk = p->chunk;
+    r.flags = p->flags;
+    return r;
+}
+
+__device__ __forceinline__ int multi_find_piece(cpiece* pieces, int npieces, uint32_t tile)
 {
     int lo = 0, hi = npieces - 1;  // last piece whose first tile is <= tile
     while (lo < hi) {
@@ -780,41 +843,73 @@ __device__ __forceinline__ int multi_find_piece(const MultiPiece* pieces, int np
 // only increase, so after a binary search for its first tile it finds the
 // next piece by scanning forward. NR > 0 fixes the rank count at compile time.
 template <class F, int OP, int NR, bool NT>
-__global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
+__device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned char* table)
 {
     using Acc = typename F::Acc;
     constexpr int E = F::kEpv;
-    const int n = NR > 0 ? NR : a.n;
-    const MultiPiece* pieces = reinterpret_cast<const MultiPiece*>(a.blob + a.pieces_offset);
-    int pidx = blockIdx.x < a.ntiles ? multi_find_piece(pieces, a.npieces, blockIdx.x) : 0;
-    for (uint32_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        while (pidx + 1 < a.npieces && pieces[pidx + 1].tile0 <= tile) ++pidx;
-        const MultiPiece& pc = pieces[pidx];
-        // The blob's pointers are read-only kernel arguments; the recv half
-        // holds device addresses the kernel writes through.
-        const uintptr_t* block = reinterpret_cast<const uintptr_t*>(a.blob) + static_cast<uint64_t>(pc.tensor) * 2 * n;
-        const void* const* send = reinterpret_cast<const void* const*>(block);
-        void* const* recv = reinterpret_cast<void* const*>(const_cast<uintptr_t*>(block + n));
+    const int n = NR > 0 ? NR : h.n;
+    // The tiles are split into S equal segments (S = rank count, like the
+    // flat kernel's chunk rows) and each segment gets every S-th workgroup,
+    // which strides through it: the workgroups in flight spread over the
+    // whole batch instead of one window of it, and every segment has the
+    // same work.
+    const uint32_t G = gridDim.x;
+    const uint32_t S = min(static_cast<uint32_t>(h.n), G);
+    const uint32_t seg = blockIdx.x % S;
+    const uint32_t step = G / S + (seg < G % S ? 1u : 0u);
+    const uint32_t L = (h.ntiles + S - 1) / S;
+    const uint32_t t_end = min(h.ntiles, (seg + 1) * L);
+    const uint32_t t_first = seg * L + blockIdx.x / S;
+    if (t_first >= t_end) return;
+    cbyte* ctable = (cbyte*)(table);
+    cpiece* pieces = (cpiece*)(ctable + h.pieces_offset);
+    // The current piece and the first tile of the next one, reloaded only
+    // when a tile crosses into another piece.
+    int pidx = multi_find_piece(pieces, h.npieces, t_first);
+    MultiPiece pc = load_piece(pieces + pidx);
+    uint32_t next0 = pidx + 1 < h.npieces ? pieces[pidx + 1].tile0 : UINT32_MAX;
+    for (uint32_t tile = t_first; tile < t_end; tile += step) {
+        if (tile >= next0) {
+            do {
+                ++pidx;
+                next0 = pidx + 1 < h.npieces ? pieces[pidx + 1].tile0 : UINT32_MAX;
+            } while (tile >= next0);
+            pc = load_piece(pieces + pidx);
+        }
+        // The table is read-only here; its recv pointers are device
+        // addresses the kernel writes through.
+        cuptr* block = (cuptr*)(ctable) + pc.ptrs;
+        const void* const* send = (const void* const*)(block);
+        void* const* recv = (void* const*)((pc.flags & kPieceInPlace) ? block : block + n);
         const int c = pc.chunk;
         const uint32_t ti = tile - pc.tile0;
         const uint64_t j_end = pc.j0 + pc.len;
-        if (pc.vec) {
-            const uint64_t vb = (pc.j0 + E - 1) / E, ve = j_end / E;
+        if (pc.flags & kPieceVec) {
+            // vector k holds elements [a0 + kE, a0 + (k+1)E): its address is
+            // base + a0 * sizeof(element) + 16k, aligned on every rank
+            const uint64_t a0 = (pc.flags >> kPieceShiftBit) & 7u;
+            const uint64_t boff = a0 * (16 / E);
+            uint64_t vb, ve;
+            piece_vectors(pc.j0, j_end, a0, E, &vb, &ve);
             const uint64_t v = vb + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
             if (v < ve) {
                 Acc acc[E];
-                fold_vec<F, OP, NR, NT>(send, c, n, v, acc);
+                fold_vec<F, OP, NR, NT>(send, c, n, v, acc, boff);
 #pragma unroll
                 for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
                 const u32x4 out = F::pack(acc);
 #pragma unroll
-                for (int r = 0; r < n; ++r) stv<NT>(recv[r], v, out);
+                for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], v * 16 + boff, out);
             }
             if (ti == 0) {
                 // elements before the first whole vector and after the last
-                const uint64_t head_end = vb * E < j_end ? vb * E : j_end;
+                const uint64_t vstart = a0 + vb * E, vend = a0 + ve * E;
+                const uint64_t head_end = vstart < j_end ? (vstart > pc.j0 ? vstart : pc.j0) : j_end;
                 const uint64_t nhead = head_end - pc.j0;
-                const uint64_t tail_start = ve * E > head_end ? ve * E : head_end;
+                // (a piece with no whole vector is all head: vend may lie
+                // past j_end then)
+                const uint64_t tail_lo = vend > head_end ? vend : head_end;
+                const uint64_t tail_start = tail_lo < j_end ? tail_lo : j_end;
                 const uint64_t ntail = j_end - tail_start;
                 if (threadIdx.x < nhead + ntail) {
                     const uint64_t i = threadIdx.x < nhead ? pc.j0 + threadIdx.x : tail_start + (threadIdx.x - nhead);
@@ -830,6 +925,12 @@ __global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
             }
         }
     }
+}
+
+template <class F, int OP, int NR, bool NT>
+__global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
+{
+    multi_body<F, OP, NR, NT>(a.h, a.blob);
 }
 
 // ---------------------------------------------------------------------------
@@ -982,7 +1083,7 @@ template <class F, int OP, bool NT>
 hipError_t multi_nr(const MultiArgs& a, int grid_x, hipStream_t s)
 {
     const dim3 grid(grid_x), block(kBlock);
-    if (a.n == 8) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);
+    if (a.h.n == 8) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
@@ -1009,10 +1110,10 @@ hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, int grid_x, hipStre
 // Per-dtype entry points, each instantiated once: the ring kernels (fused,
 // stepwise reduce-scatter, multi-tensor) in dtype_<name>.hip and the tree
 // kernels in tree_<name>.hip, so the build compiles them in parallel.
-#define AR_RING_INSTANTIATIONS(F, EXTERN)                                                                   \
-    EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t);  \
-    EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t); \
-    EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, dim3, hipStream_t);                   \
+#define AR_RING_INSTANTIATIONS(F, EXTERN)                                                                       \
+    EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t);      \
+    EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t);     \
+    EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, dim3, hipStream_t);                       \
     EXTERN template hipError_t multi_op<F>(const MultiArgs&, ar_op_t, bool, int, hipStream_t);
 #define AR_TREE_INSTANTIATIONS(F, EXTERN)                                                           \
     EXTERN template hipError_t tree_op<F>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t); \

@@ -22,12 +22,15 @@ def run_multi(comm, sizes, dtype, op, seed, inplace=False, offset=0):
     flat = gu.make_inputs(n, total, dtype, op, seed=seed)  # the bucket each rank would hold
     send, recv = [], []
     off = 0
-    for c in sizes:
-        srow = [gu.RankBuf(c, dtype, offset=offset) for _ in range(n)]
+    # offset: bytes added to every buffer, or a function (tensor, rank, side)
+    # -> bytes, side 0 = send, 1 = recv
+    at = offset if callable(offset) else (lambda t, r, side: offset)
+    for t, c in enumerate(sizes):
+        srow = [gu.RankBuf(c, dtype, offset=at(t, r, 0)) for r in range(n)]
         for r in range(n):
             srow[r].view.copy_(flat[r][off:off + c])
         send.append(srow)
-        recv.append(srow if inplace else [gu.RankBuf(c, dtype, offset=offset) for _ in range(n)])
+        recv.append(srow if inplace else [gu.RankBuf(c, dtype, offset=at(t, r, 1)) for r in range(n)])
         off += c
     ar.ar_all_reduce_multi(comm, [[b.ptr() for b in row] for row in send], [[b.ptr() for b in row] for row in recv],
                            sizes, dtype, op)
@@ -65,6 +68,24 @@ def test_multi_matches_flat_bucket(n, dtype):
             check(comm, sizes, dtype, op, seed=len(sizes) + n)
             check(comm, sizes, dtype, op, seed=9, inplace=True)
             check(comm, sizes, dtype, op, seed=11, offset=gu.ESIZE[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i32"])
+def test_multi_shifted_and_mixed_alignment(dtype):
+    """Every rank's tensor at the same offset from a 16-byte boundary (each
+    offset in turn): 16-byte vectors shifted past the first elements. Ranks
+    or send/recv at different offsets: the element path. Sizes below one
+    vector, across chunk boundaries and over several tiles."""
+    e = gu.ESIZE[dtype]
+    epv = gu.EPV[dtype]
+    sizes = [1, epv - 1, epv + 1, 3 * epv + 2, 2 * 256 * epv + 5, 0, 7, 4 * 256 * epv + epv - 1, 2]
+    for n in (3, 8):
+        with ar.Comm(n, 0) as comm:
+            for k in range(epv):
+                check(comm, sizes, dtype, "sum", seed=100 + k, offset=k * e)
+                check(comm, sizes, dtype, "max", seed=200 + k, offset=k * e, inplace=True)
+            check(comm, sizes, dtype, "sum", seed=300, offset=lambda t, r, side: ((t + r) % epv) * e)
+            check(comm, sizes, dtype, "prod", seed=301, offset=lambda t, r, side: side * e)
 
 
 def test_multi_many_tensors_many_launches():
@@ -124,3 +145,85 @@ def test_bucket64_mixed_tensors_full_size(op):
         print(f"{len(sizes)} tensors per rank")
     del bufs, flat
     torch.cuda.empty_cache()
+
+
+def _multi_case(n, sizes, dtype, op, seed):
+    """Send tensors filled from a seeded flat bucket, empty recv tensors, and
+    the oracle's flat-bucket result."""
+    total = sum(sizes)
+    flat = gu.make_inputs(n, total, dtype, op, seed=seed)
+    exp = oracle.fold_all_reduce([gu.host(x) for x in flat], dtype, op)
+    send, recv, off = [], [], 0
+    for c in sizes:
+        row = [gu.RankBuf(c, dtype) for _ in range(n)]
+        for r in range(n):
+            row[r].view.copy_(flat[r][off:off + c])
+        send.append(row)
+        recv.append([gu.RankBuf(c, dtype) for _ in range(n)])
+        off += c
+    return send, recv, exp
+
+
+def _check_multi(recv, exp, dtype, what):
+    for r in range(len(exp)):
+        got = np.concatenate([gu.host(row[r].view) for row in recv])
+        gu.assert_same(got, exp[r], dtype, f"{what} rank {r}")
+
+
+def _ptrs(rows):
+    return [[b.ptr() for b in row] for row in rows]
+
+
+@pytest.mark.parametrize("n", [8, 64])
+def test_multi_captured_replays(n):
+    """Captured in torch.cuda.graph (3 tensors per launch at 64 ranks),
+    replayed four times with eager multi-tensor calls between replays: every
+    replay and every eager call equals the oracle."""
+    dtype, op = "bf16", "sum"
+    sizes = [5000, 1, 40000, 0, 8 * 1024 + 3, 777, 30000, 12, 65536]
+    send, recv, exp = _multi_case(n, sizes, dtype, op, seed=11)
+    send2, recv2, exp2 = _multi_case(n, sizes[::-1], dtype, op, seed=12)
+    with ar.Comm(n, 0) as comm:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            ar.ar_all_reduce_multi(comm, _ptrs(send), _ptrs(recv), sizes, dtype, op, "fused", s)
+        for trial in range(4):
+            for row in recv + recv2:
+                for b in row:
+                    b.view.fill_(0)
+            torch.cuda.synchronize()
+            g.replay()
+            ar.ar_all_reduce_multi(comm, _ptrs(send2), _ptrs(recv2), sizes[::-1], dtype, op)
+            torch.cuda.synchronize()
+            _check_multi(recv, exp, dtype, f"replay {trial}")
+            _check_multi(recv2, exp2, dtype, f"eager between replays {trial}")
+
+
+def test_multi_many_launches_and_two_streams():
+    """Many small tensors (1500 per rank: dozens of kernel-argument batches),
+    calls of different sizes in a row, and two calls in flight on two
+    streams at once: every result equals the oracle."""
+    n, dtype, op = 8, "f32", "max"
+    small = [1000, 2000]
+    many = [64 + (t % 7) * 1000 for t in range(1500)]
+    big = [4 << 20, 3 << 20]
+    with ar.Comm(n, 0) as comm:
+        cases = []
+        for k, sizes in enumerate((small, many, small)):
+            send, recv, exp = _multi_case(n, sizes, dtype, op, seed=30 + k)
+            ar.ar_all_reduce_multi(comm, _ptrs(send), _ptrs(recv), sizes, dtype, op)
+            cases.append((recv, exp, f"case {k}"))
+        torch.cuda.synchronize()
+        for recv, exp, what in cases:
+            _check_multi(recv, exp, dtype, what)
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        sa, ra, ea = _multi_case(n, big, dtype, op, seed=40)
+        sb, rb, eb = _multi_case(n, many, dtype, op, seed=41)
+        torch.cuda.synchronize()
+        ar.ar_all_reduce_multi(comm, _ptrs(sa), _ptrs(ra), big, dtype, op, "fused", s1)
+        ar.ar_all_reduce_multi(comm, _ptrs(sb), _ptrs(rb), many, dtype, op, "fused", s2)
+        torch.cuda.synchronize()
+        _check_multi(ra, ea, dtype, "stream 1")
+        _check_multi(rb, eb, dtype, "stream 2")
