@@ -330,6 +330,9 @@ __device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, 
     }
 }
 
+// Per-row rotation of the fused sweep, in tiles (odd, not a power of two).
+constexpr uint64_t kRowSkewTiles = 37;
+
 // grid = (blocks per chunk, n chunks). Workgroup row y handles chunk y, so the
 // ring order (which rank's buffer is loaded k-th) is uniform per workgroup.
 // All-reduce (SCATTER = false) writes the result to every rank; reduce-scatter
@@ -347,8 +350,18 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     chunk_range(a.q, a.count, c, lo, hi);
     const uint64_t nv = (hi - lo) / E;
     const uint64_t v0 = lo / E;  // exact: the host requires q % E == 0
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
-    for (uint64_t v = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x; v < nv; v += stride) {
+    // Tiles of kBlock vectors, grid-strided. Row c starts its sweep rotated
+    // by c * kRowSkewTiles tiles: when chunk and rank buffers sit at
+    // power-of-two distances, rows that move in lock step would otherwise hit
+    // the same HBM banks at the same time (measured +1% with separate rank
+    // allocations, +4% with rank buffers at 256 MiB strides in one
+    // allocation). Each element's fold is unchanged.
+    const uint64_t ntiles = (nv + kBlock - 1) / kBlock;
+    const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint64_t tr = t + rot < ntiles ? t + rot : t + rot - ntiles;
+        const uint64_t v = tr * kBlock + threadIdx.x;
+        if (v >= nv) continue;
         Acc acc[E];
         fold_vec<F, OP, NR, NT>(a.send, c, n, v0 + v, acc);
 #pragma unroll
