@@ -57,7 +57,7 @@ WORKLOADS = {
                 "bucket8: 8 virtual ranks x 256 MiB fp32 bucket, uniform[-1,1), MAX, in place"),
 }
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4}
-CPU_WINDOW_LOG2 = 26  # elements per rank in the CPU oracle's window
+CPU_WINDOW_LOG2 = 27  # elements per rank in the CPU oracle's window (about 10 s of oracle work)
 
 
 def alpha_beta_time(nranks: int, msg_bytes: float, alpha_s: float, beta_bytes_per_s: float):
@@ -104,21 +104,38 @@ def load_traffic(workload: str, mode: str):
     return float(t.group(1))
 
 
-def cpu_baseline(nranks: int, dtype: str, op: str, workload: str):
-    """The oracle's literal ring on the first 2^26 elements per rank of the
-    same workload (seeded the same way), timed on one host thread."""
+def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "all_reduce"):
+    """The oracle on a window of the same workload (2^CPU_WINDOW_LOG2
+    elements per rank on the large side, seeded the same way), timed on one
+    host thread: the literal ring for all-reduce, the oracle's reduce-scatter,
+    all-gather or all-to-all otherwise. algbw convention as the GPU line."""
     import oracle
     import synthetic
     count = 1 << CPU_WINDOW_LOG2
     wl = workload if workload in synthetic.WORKLOAD_IDS else "sweep"
-    xs = [synthetic.to_numpy(t) for t in synthetic.rank_inputs(wl, nranks, count, dtype, op=op)]
+    in_count = count // nranks if coll == "all_gather" else count
+    # generated on the device (fast), copied to host memory before timing
+    import torch
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    xs = [synthetic.to_numpy(t) for t in synthetic.rank_inputs(wl, nranks, in_count, dtype, device=dev, op=op)]
     t0 = time.perf_counter()
-    oracle.ring_all_reduce(xs, dtype, op)
+    if coll == "all_reduce":
+        oracle.ring_all_reduce(xs, dtype, op)
+        what = "literal ring (N-1 reduce-scatter + N-1 all-gather steps)"
+    elif coll == "reduce_scatter":
+        oracle.reduce_scatter(xs, dtype, op)
+        what = "reduce-scatter"
+    elif coll == "all_gather":
+        oracle.all_gather(xs, dtype)
+        what = "all-gather"
+    else:
+        oracle.all_to_all(xs, dtype)
+        what = "all-to-all"
     dt = time.perf_counter() - t0
     s_bytes = count * ESIZE[dtype]
     return {"value": s_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{nranks} ranks x 2^{CPU_WINDOW_LOG2} {dtype} elements per rank ({s_bytes / 2**20:.0f} MiB), "
-                      f"literal ring (N-1 reduce-scatter + N-1 all-gather steps), {op}, single thread",
+                      f"{what}, {op}, single thread",
             "seconds": dt}
 
 
@@ -217,6 +234,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="grad7b", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused", choices=["fused", "stepwise", "graph", "tree", "tree_stepwise"])
+    ap.add_argument("--collective", default="all_reduce",
+                    choices=["all_reduce", "reduce_scatter", "all_gather", "all_to_all"],
+                    help="the collective to time on the workload's rank buffers: reduce_scatter takes count "
+                         "elements per rank in and count/N out, all_gather count/N in and count out, all_to_all "
+                         "count in and out (out of place)")
     ap.add_argument("--multi", action="store_true",
                     help="bucket64/bucket8: reduce the bucket as its mixed-size tensors with ar_all_reduce_multi")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -254,6 +276,13 @@ def main():
     comm = ar.Comm(n, 0)
     stream = torch.cuda.current_stream()
     sizes = None
+    coll = args.collective
+    if coll != "all_reduce":
+        if args.multi or args.mode not in ("fused", "stepwise", "graph") or count % n:
+            print("bench.py: --collective other than all_reduce takes a ring mode, no --multi, and a count "
+                  "divisible by the rank count", file=sys.stderr)
+            sys.exit(2)
+        desc += f"; {coll}, out of place"
     if args.multi:
         if args.workload not in ("bucket64", "bucket8") or args.mode != "fused":
             print("bench.py: --multi applies to --workload bucket64 or bucket8 in fused mode", file=sys.stderr)
@@ -266,21 +295,40 @@ def main():
     # warm if it ran on one buffer set back to back; rotate K sets so that
     # K*N*S >= 1 GiB and every call reads from HBM. The warm figure on one
     # set is reported beside it, labelled.
-    sets = 1 if n * s_bytes > LLC_BYTES else -(-ROTATE_BYTES // (n * s_bytes))
+    foot = {"all_reduce": n, "all_to_all": 2 * n}.get(coll, n + 1) * s_bytes  # distinct bytes per call
+    sets = 1 if foot > LLC_BYTES else -(-ROTATE_BYTES // foot)
 
     def timed_pass(measure_warm: bool):
         """Allocate and fill the rank buffers, warm up, time exactly K steps
         (an event after each step gives the per-step times)."""
         print(f"[bench] generating {desc}" + (f" ({sets} rotating buffer sets)" if sets > 1 else ""),
               file=sys.stderr, flush=True)
-        bufsets = [synthetic.rank_inputs(wl, n, count, dtype, device="cuda", op=op, salt=k) for k in range(sets)]
+        # the input side: count elements per rank, or count/N for all-gather
+        in_count = count // n if coll == "all_gather" else count
+        out_count = {"all_reduce": count, "reduce_scatter": count // n}.get(coll, count)
+        bufsets = [synthetic.rank_inputs(wl, n, in_count, dtype, device="cuda", op=op, salt=k) for k in range(sets)]
+        outsets = None if coll == "all_reduce" else \
+            [[torch.empty(out_count, dtype=bufsets[0][0].dtype, device="cuda") for _ in range(n)] for _ in range(sets)]
         ws = None
-        need = ar.ar_workspace_bytes(ar.AR_COLL_ALL_REDUCE, n, count, dtype, args.mode)
+        cenum = {"all_reduce": ar.AR_COLL_ALL_REDUCE, "reduce_scatter": ar.AR_COLL_REDUCE_SCATTER,
+                 "all_gather": ar.AR_COLL_ALL_GATHER, "all_to_all": ar.AR_COLL_ALL_TO_ALL}[coll]
+        wcount = count // n if coll == "reduce_scatter" else count
+        need = ar.ar_workspace_bytes(cenum, n, wcount, dtype, args.mode)
         if need:
             ws = torch.empty(need, dtype=torch.uint8, device="cuda")
             ar.ar_comm_set_workspace(comm, ws)
         ptrsets = [[b.data_ptr() for b in bufs] for bufs in bufsets]
-        if sizes is None:
+        outptrs = None if outsets is None else [[b.data_ptr() for b in bufs] for bufs in outsets]
+        if coll != "all_reduce":
+            def step(i):
+                p, q = ptrsets[i % sets], outptrs[i % sets]
+                if coll == "reduce_scatter":
+                    ar.ar_reduce_scatter(comm, p, q, count // n, dtype, op, args.mode, stream)
+                elif coll == "all_gather":
+                    ar.ar_all_gather(comm, p, q, count // n, dtype, args.mode, stream)
+                else:
+                    ar.ar_all_to_all(comm, p, q, count // n, dtype, args.mode, stream)
+        elif sizes is None:
             def step(i):
                 p = ptrsets[i % sets]
                 ar.ar_all_reduce(comm, p, p, count, dtype, op, args.mode, stream)
@@ -312,7 +360,7 @@ def main():
         ms_, per_step = run(args.steps, True)
         warm = run(args.steps, False)[0] if measure_warm and sets > 1 else None
         ar.ar_comm_set_workspace(comm, None)
-        del bufsets, ptrsets, ws
+        del bufsets, ptrsets, outsets, outptrs, ws
         torch.cuda.empty_cache()
         return ms_, per_step, warm
 
@@ -325,13 +373,18 @@ def main():
     ms, per_step, warm_ms = timed_pass(True)
     per_step.sort()
 
+    # nccl-tests conventions: algbw = S / T with S the per-rank buffer of
+    # count elements (the input of reduce-scatter and all-to-all, the output
+    # of all-gather); busbw = algbw * 2(N-1)/N for all-reduce, (N-1)/N else.
     algbw = s_bytes / (ms * 1e-3) / 1e9
-    busbw = algbw * 2 * (n - 1) / n
-    # fused: one launch per step; stepwise: 2(N-1) launches, reported against
-    # the same algorithmic bytes so the two modes compare directly.
-    alg_bytes = 2 * n * s_bytes
+    busbw = algbw * (2 if coll == "all_reduce" else 1) * (n - 1) / n
+    # Algorithmic HBM bytes per call: all-reduce and all-to-all read N*S and
+    # write N*S; reduce-scatter reads N*S and writes S (N blocks of S/N);
+    # all-gather reads S (N blocks of S/N) and writes N*S. Stepwise modes
+    # move more and are reported against the same bytes, so modes compare.
+    alg_bytes = (2 * n if coll in ("all_reduce", "all_to_all") else n + 1) * s_bytes
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, args.mode)
+    traffic = load_traffic(args.workload, args.mode) if coll == "all_reduce" and not args.multi else None
     result = {
         "metric": METRIC,
         "value": round(algbw, 3),
@@ -349,7 +402,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": desc, "nranks": n, "count_per_rank": count, "bytes_per_rank": s_bytes, "op": op,
-                   "mode": args.mode, "accumulate": "f32" if dtype in ("f16", "bf16") else dtype,
+                   "mode": args.mode, "collective": coll,
+                   "accumulate": "f32" if dtype in ("f16", "bf16") else dtype,
                    "parallelism": f"{n} virtual ranks on 1 GPU"},
         "busbw": round(busbw, 3),
         "hbm_gbps": round(achieved, 1),
@@ -365,7 +419,7 @@ def main():
                                     "note": "one buffer set called back to back; served from the last-level cache"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload)
+        result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload, coll)
     print(json.dumps(result), flush=True)
 
 
