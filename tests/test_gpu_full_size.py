@@ -127,3 +127,55 @@ def test_bucket64_ops(op):
             check_sampled(comm, bufs, "f32", op, mode, seed=salt)
             del bufs
             free()
+
+
+def test_grad7b_reduce_scatter_then_all_gather():
+    """The export shapes `bench.py --collective` times at the 7B-gradient
+    size: reduce-scatter of 8 x 7e9 fp16 (14 GB in per rank, 1.75 GB out),
+    AVG, out of place, then all-gather of the reduced blocks back into the
+    14 GB buffers. Sampled elements (random, every block boundary, the ends)
+    against the oracle's all-reduce of those elements: block r of the
+    reduce-scatter is chunk r of the all-reduce, and every all-gathered rank
+    holds the all-reduce."""
+    n, count = 8, 7_000_000_000
+    rc = count // n
+    with ar.Comm(n, 0) as comm:
+        send = synthetic.rank_inputs("grad7b", n, count, "f16", device="cuda", salt=2)
+        recv = [torch.empty(rc, dtype=torch.float16, device="cuda") for _ in range(n)]
+        idx = sample_indices(n, count, np.random.default_rng(6))
+        exp = oracle.all_reduce_elements(gather(send, idx), idx, count, "f16", "avg")
+        ar.ar_reduce_scatter(comm, [b.data_ptr() for b in send], [b.data_ptr() for b in recv], rc, "f16", "avg",
+                             "fused")
+        torch.cuda.synchronize()
+        it = torch.from_numpy(idx).cuda()
+        got = torch.empty(idx.size, dtype=torch.float16, device="cuda")
+        for r in range(n):
+            sel = (it // rc) == r
+            got[sel] = recv[r][it[sel] - r * rc]
+        gu.assert_same(synthetic.to_numpy(got), exp, "f16", "reduce-scatter sampled")
+        ar.ar_all_gather(comm, [b.data_ptr() for b in recv], [b.data_ptr() for b in send], rc, "f16", "fused")
+        torch.cuda.synchronize()
+        after = gather(send, idx)
+        for r in range(n):
+            gu.assert_same(np.ascontiguousarray(after[:, r]), exp, "f16", f"all-gather rank {r} sampled")
+        for r in range(1, n):
+            assert torch.equal(send[r].view(torch.int16), send[0].view(torch.int16)), f"rank {r} differs"
+    del send, recv
+    free()
+
+
+def test_all_to_all_256mib_fp32_full_compare():
+    """All-to-all of 8 x 256 MiB fp32 (the `--collective all_to_all` sweep
+    point), every element against the oracle's transpose."""
+    n, count = 8, 67_108_864
+    blk = count // n
+    with ar.Comm(n, 0) as comm:
+        send = synthetic.rank_inputs("sweep", n, count, "f32", device="cuda", salt=9)
+        recv = [torch.empty(count, dtype=torch.float32, device="cuda") for _ in range(n)]
+        exp = oracle.all_to_all([gu.host(b) for b in send], "f32")
+        ar.ar_all_to_all(comm, [b.data_ptr() for b in send], [b.data_ptr() for b in recv], blk, "f32", "fused")
+        torch.cuda.synchronize()
+        for p in range(n):
+            gu.assert_same(gu.host(recv[p]), exp[p], "f32", f"all-to-all rank {p}")
+    del send, recv
+    free()
