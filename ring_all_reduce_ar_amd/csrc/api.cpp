@@ -184,14 +184,20 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
     return f;
 }
 
-// Workgroups per CU for the fused reduction, as measured on MI355X with
-// 16-byte vectors: at 8 ranks 16 per CU is ~2% faster up to 128 MiB per rank
-// and 8 per CU ~2% faster for multi-GB ranks; at 64 ranks 16 per CU is ~3%
-// faster (256 MiB per rank).
-int fused_per_cu(size_t bytes_per_rank, int nranks)
+// Workgroups per CU for the fused all-reduce, from sweeps of 2..16 per CU in
+// one process on MI355X (fp32 SUM, 64 MiB..1 GiB per rank, N = 2..64; fp16
+// at 14 GB per rank):
+//  - N <= 4: 2 per CU beat 8 by 4-10 points once the data exceeds the
+//    last-level cache; cache-resident calls are within 2 points of each other
+//    and take 8;
+//  - 5 <= N <= 32: 4 per CU is best or within 1 point (the 8 x 14 GB fp16
+//    workload: 75.0% against 74.1% at 8);
+//  - N > 32: 16 per CU up to 128 MiB per rank, 12 above.
+int fused_per_cu(size_t bytes_per_rank, int nranks, bool cached)
 {
-    if (nranks >= 32) return 16;
-    return bytes_per_rank <= (size_t(128) << 20) ? 16 : 8;
+    if (nranks <= 4) return cached ? 8 : 2;
+    if (nranks <= 32) return 4;
+    return bytes_per_rank <= (size_t(128) << 20) ? 16 : 12;
 }
 
 // Records the start of a call and the end of each step when timing is on.
@@ -492,7 +498,10 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         a.count = count;
         a.q = count;
         a.n = n;
-        const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, fused_per_cu(count * e, n));
+        // one row over the whole buffer: 16 workgroups per CU up to 128 MiB
+        // per rank or at 32+ ranks, 8 above (measured ±2-3% at 8 ranks)
+        const int per_cu = (count * e <= (size_t(128) << 20) || n >= 32) ? 16 : 8;
+        const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, per_cu);
         const bool nt = use_nt(footprint(n, sendbufs, recvbufs, count * e, count * e));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, nt, gx, s);
@@ -553,13 +562,17 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     // Ring plan: q = ceil(count / n); chunk c = [c*q, min((c+1)*q, count)).
     const uint64_t q = ceil_div(count, static_cast<uint64_t>(n));
     const uint64_t epv = 16 / e;
-    const bool vec = all_aligned16(n, sendbufs, recvbufs) && (n == 1 || q % epv == 0);
+    // The fused kernel takes 16-byte vectors whenever every pointer is
+    // aligned (chunks that start inside a vector get element-wise heads and
+    // tails); the stepwise steps also need whole-vector chunks.
+    const bool fvec = all_aligned16(n, sendbufs, recvbufs);
+    const bool vec = fvec && (n == 1 || q % epv == 0);
     DeviceGuard g(comm->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
     if (comm->debug)
-        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%d q=%llu vec=%d\n", n, count,
+        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%d q=%llu vec=%d/%d\n", n, count,
                      dtype_name(dtype), static_cast<int>(op), static_cast<int>(mode),
-                     static_cast<unsigned long long>(q), vec ? 1 : 0);
+                     static_cast<unsigned long long>(q), fvec ? 1 : 0, vec ? 1 : 0);
 
     if (!stepwise) {
         ar::ReduceArgs a{};
@@ -568,9 +581,9 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         a.q = q;
         a.n = n;
         const bool nt = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
-        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n));
+        const int gx = grid_for(comm, fvec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n, !nt));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, gx, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, fvec, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }

@@ -397,43 +397,58 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     const int c = blockIdx.y;
     uint64_t lo, hi;
     chunk_range(a.q, a.count, c, lo, hi);
-    const uint64_t nv = (hi - lo) / E;
-    const uint64_t v0 = lo / E;  // exact: the host requires q % E == 0
+    // The chunk's whole 16-byte vectors: every rank pointer is 16-byte
+    // aligned, so vector v holds elements [vE, vE + E) of every buffer. A
+    // chunk that starts or ends inside a vector (q not a multiple of E) has
+    // fewer than E head and tail elements, done one by one below. The
+    // reduce-scatter layout (SCATTER) needs q % E == 0, which the host checks.
+    const uint64_t v0 = (lo + E - 1) / E;
+    const uint64_t v1 = hi / E;
+    const uint64_t nv = v1 > v0 ? v1 - v0 : 0;
     // Tiles of kBlock vectors, grid-strided. Row c starts its sweep rotated
     // by c * kRowSkewTiles tiles: when chunk and rank buffers sit at
     // power-of-two distances, rows that move in lock step would otherwise hit
     // the same HBM banks at the same time (measured +1% with separate rank
     // allocations, +4% with rank buffers at 256 MiB strides in one
     // allocation). Each element's fold is unchanged.
-    const uint64_t ntiles = (nv + kBlock - 1) / kBlock;
-    const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
     if constexpr (SCATTER && NR > 0) {
         // Reduce-scatter reads N vectors per vector it writes: two tiles per
         // iteration keep 2*NR loads in flight per thread (measured +2-6%).
+        const uint64_t ntiles = (nv + kBlock - 1) / kBlock;
+        const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
         fused_scatter_x2<F, OP, NR, NT>(a, c, v0, nv, ntiles, rot);
     } else {
+        // Tiles are the buffer's aligned 4 KiB blocks (kBlock vectors), so a
+        // wave's 1 KiB never straddles an extra cache line; the chunk's first
+        // and last tiles may be partial.
+        const uint64_t tbase = v0 / kBlock;
+        const uint64_t ntiles = nv ? (v1 - 1) / kBlock - tbase + 1 : 0;
+        const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
         for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
             const uint64_t tr = t + rot < ntiles ? t + rot : t + rot - ntiles;
-            const uint64_t v = tr * kBlock + threadIdx.x;
-            if (v >= nv) continue;
+            const uint64_t v = (tbase + tr) * kBlock + threadIdx.x;
+            if (v < v0 || v >= v1) continue;
             Acc acc[E];
-            fold_vec<F, OP, NR, NT>(a.send, c, n, v0 + v, acc);
+            fold_vec<F, OP, NR, NT>(a.send, c, n, v, acc);
 #pragma unroll
             for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
             const u32x4 out = F::pack(acc);
             if constexpr (SCATTER) {
-                stv<NT>(a.recv[c], v, out);
+                stv<NT>(a.recv[c], v - v0, out);
             } else {
 #pragma unroll
-                for (int r = 0; r < n; ++r) stv<NT>(a.recv[r], v0 + v, out);
+                for (int r = 0; r < n; ++r) stv<NT>(a.recv[r], v, out);
             }
         }
     }
-    // A chunk whose length is not a whole number of vectors (only the last
-    // non-empty one) finishes its < E trailing elements here.
+    // Head [lo, v0 E) and tail [v1 E, hi): fewer than E elements each.
     if (blockIdx.x == 0) {
-        const uint64_t i = lo + nv * E + threadIdx.x;
-        if (i < hi) {
+        const uint64_t head_end = v0 * E < hi ? v0 * E : hi;
+        const uint64_t nhead = head_end - lo;
+        const uint64_t tail_start = v1 * E > head_end ? v1 * E : head_end;
+        const uint64_t ntail = hi - tail_start;
+        if (threadIdx.x < nhead + ntail) {
+            const uint64_t i = threadIdx.x < nhead ? lo + threadIdx.x : tail_start + (threadIdx.x - nhead);
             const Acc x = finalize<OP>(fold_elem<F, OP>(a.send, c, n, i), n);
             if constexpr (SCATTER) {
                 F::st(a.recv[c], i - lo, x);
