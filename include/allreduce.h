@@ -162,9 +162,11 @@ ar_result_t ar_comm_set_workspace(ar_comm_t comm, void* dev_ptr, size_t bytes);
  * between any two of the 2*nranks buffers (or the workspace) is
  * INVALID_ARGUMENT. Ring-mode fp16/bf16 needs a workspace of
  * ar_workspace_bytes(...) bytes, else INVALID_ARGUMENT. Pointers must be
- * aligned to the element size (else INVALID_ARGUMENT); 16-byte alignment
- * with q a multiple of 16/sizeof(dtype) selects the vector kernels, other
- * layouts take element-wise kernels with the same results. */
+ * aligned to the element size (else INVALID_ARGUMENT). With every pointer
+ * 16-byte aligned the fused kernel moves 16-byte vectors (chunk ends that
+ * fall inside a vector are done element by element); the stepwise steps
+ * also need q to be a multiple of 16/sizeof(dtype). Other layouts take
+ * element-wise kernels. The results are the same bits either way. */
 ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
                           ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
 
