@@ -179,3 +179,18 @@ def test_all_to_all_256mib_fp32_full_compare():
             gu.assert_same(gu.host(recv[p]), exp[p], "f32", f"all-to-all rank {p}")
     del send, recv
     free()
+
+
+@pytest.mark.parametrize("n,count,dtype", [(3, 89_478_485, "f32"), (5, 134_217_727, "f16"), (7, 40_000_003, "bf16"),
+                                           (2, 268_435_456, "f32"), (4, 100_000_001, "i32")])
+def test_odd_rank_counts_large(n, count, dtype):
+    """Rank counts and sizes whose chunk length is not a multiple of the
+    16-byte vector width (chunks start inside a vector), and the 2- and
+    4-rank launch shapes, at 100 MiB-1 GiB per rank: fused, in place,
+    sampled elements (every chunk boundary +-2 among them) against the
+    oracle, all ranks identical."""
+    with ar.Comm(n, 0) as comm:
+        bufs = synthetic.rank_inputs("sweep", n, count, dtype, device="cuda", salt=n)
+        check_sampled(comm, bufs, dtype, "sum", "fused", seed=n)
+        del bufs
+    free()
