@@ -562,17 +562,15 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     // Ring plan: q = ceil(count / n); chunk c = [c*q, min((c+1)*q, count)).
     const uint64_t q = ceil_div(count, static_cast<uint64_t>(n));
     const uint64_t epv = 16 / e;
-    // The fused kernel takes 16-byte vectors whenever every pointer is
-    // aligned (chunks that start inside a vector get element-wise heads and
-    // tails); the stepwise steps also need whole-vector chunks.
-    const bool fvec = all_aligned16(n, sendbufs, recvbufs);
-    const bool vec = fvec && (n == 1 || q % epv == 0);
+    // 16-byte vectors whenever every pointer is aligned; chunks that start
+    // or end inside a vector get element-wise heads and tails.
+    const bool vec = all_aligned16(n, sendbufs, recvbufs);
     DeviceGuard g(comm->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
     if (comm->debug)
-        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%d q=%llu vec=%d/%d\n", n, count,
+        std::fprintf(stderr, "[allreduce] all_reduce n=%d count=%zu dtype=%s op=%d mode=%d q=%llu vec=%d\n", n, count,
                      dtype_name(dtype), static_cast<int>(op), static_cast<int>(mode),
-                     static_cast<unsigned long long>(q), fvec ? 1 : 0, vec ? 1 : 0);
+                     static_cast<unsigned long long>(q), vec ? 1 : 0);
 
     if (!stepwise) {
         ar::ReduceArgs a{};
@@ -581,9 +579,9 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         a.q = q;
         a.n = n;
         const bool nt = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
-        const int gx = grid_for(comm, fvec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n, !nt));
+        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n, !nt));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, fvec, nt, gx, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -606,7 +604,7 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     ca.qb = q * e;
     ca.n = n;
     ca.shift = 0;
-    const bool cvec = all_aligned16(n, sendbufs, recvbufs) && (ca.qb % 16 == 0);
+    const bool cvec = vec;
     const int gx_ag = grid_for(comm, cvec ? ceil_div(ca.qb, 16) : ceil_div(ca.qb, 2), n);
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int st = 0; st < n - 1; ++st) {

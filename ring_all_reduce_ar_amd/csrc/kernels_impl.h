@@ -584,9 +584,13 @@ __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
     chunk_range(a.q, a.count, c, lo, hi);
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    uint64_t done = lo;
     if constexpr (VEC) {
-        const uint64_t nv = (hi - lo) / E, v0 = lo / E;
+        // The chunk's whole 16-byte vectors (rank pointers and the workspace
+        // are 16-byte aligned); the < E elements before the first and after
+        // the last are done one by one. The reduce-scatter layout (scatter)
+        // needs q % E == 0, which the host checks.
+        const uint64_t v0 = (lo + E - 1) / E, v1 = hi / E;
+        const uint64_t nv = v1 > v0 ? v1 - v0 : 0;
         for (uint64_t v = t0; v < nv; v += stride) {
             const uint64_t vi = v0 + v;
             Acc loc[E], in[E];
@@ -607,8 +611,15 @@ __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
                 st16(a.recv[r], vi, F::pack(loc));
             }
         }
-        done = lo + nv * E;
-        if (blockIdx.x == 0 && done + threadIdx.x < hi) rs_elem<F, OP>(a, r, left, c, lo, done + threadIdx.x);
+        if (blockIdx.x == 0) {
+            const uint64_t head_end = v0 * E < hi ? v0 * E : hi;
+            const uint64_t nhead = head_end - lo;
+            const uint64_t tail_start = v1 * E > head_end ? v1 * E : head_end;
+            const uint64_t ntail = hi - tail_start;
+            if (threadIdx.x < nhead + ntail)
+                rs_elem<F, OP>(a, r, left, c, lo,
+                               threadIdx.x < nhead ? lo + threadIdx.x : tail_start + (threadIdx.x - nhead));
+        }
     } else {
         for (uint64_t i = lo + t0; i < hi; i += stride) rs_elem<F, OP>(a, r, left, c, lo, i);
     }
@@ -630,16 +641,22 @@ __global__ __launch_bounds__(kBlock) void copy_step(const CopyArgs a)
     char* dst = static_cast<char*>(a.recv[r]);
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    uint64_t done = lo;
     if constexpr (VEC) {
-        const uint64_t nv = (hi - lo) / 16, v0 = lo / 16;
+        // whole 16-byte vectors of the chunk, then the < 16 bytes before and
+        // after them in 2-byte units (chunk ends are multiples of the element
+        // size, at least 2)
+        const uint64_t v0 = (lo + 15) / 16, v1 = hi / 16;
+        const uint64_t nv = v1 > v0 ? v1 - v0 : 0;
         for (uint64_t v = t0; v < nv; v += stride) st16(dst, v0 + v, ld16(src, v0 + v));
-        done = lo + nv * 16;
         if (blockIdx.x != 0) return;
-        for (uint64_t b = done + 2 * threadIdx.x; b < hi; b += 2 * kBlock)
+        const uint64_t head_end = v0 * 16 < hi ? v0 * 16 : hi;
+        const uint64_t tail_start = v1 * 16 > head_end ? v1 * 16 : head_end;
+        for (uint64_t b = lo + 2 * threadIdx.x; b < head_end; b += 2 * kBlock)
+            *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
+        for (uint64_t b = tail_start + 2 * threadIdx.x; b < hi; b += 2 * kBlock)
             *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
     } else {
-        for (uint64_t b = done + 2 * t0; b < hi; b += 2 * stride)
+        for (uint64_t b = lo + 2 * t0; b < hi; b += 2 * stride)
             *reinterpret_cast<uint16_t*>(dst + b) = *reinterpret_cast<const uint16_t*>(src + b);
     }
 }
