@@ -118,6 +118,26 @@ struct Interval {
     int rank;
 };
 
+// Sorts `iv` by start. An interval overlaps an earlier one exactly when it
+// starts before the largest end seen so far (empty intervals overlap
+// nothing); on the first such pair returns true with *a the later interval
+// and *b the earlier one.
+bool find_overlap(std::vector<Interval>& iv, size_t* a, size_t* b)
+{
+    std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) { return x.lo < y.lo; });
+    size_t last = SIZE_MAX;  // the interval with the largest end so far
+    for (size_t i = 0; i < iv.size(); ++i) {
+        if (iv[i].hi == iv[i].lo) continue;
+        if (last != SIZE_MAX && iv[i].lo < iv[last].hi) {
+            *a = i;
+            *b = last;
+            return true;
+        }
+        if (last == SIZE_MAX || iv[i].hi > iv[last].hi) last = i;
+    }
+    return false;
+}
+
 // The 2n rank buffers (plus the workspace) must not overlap, except that a
 // rank's send buffer may sit at `inplace_off` bytes into its recv buffer
 // (all-reduce: 0; all-gather: r*sendbytes) or its recv buffer at
@@ -148,12 +168,10 @@ ar_result_t check_buffers(int n, const void* const send[], void* const recv[], s
         }
     }
     if (ws_need) iv.push_back({reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + ws_need, "workspace", -1});
-    std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
-    for (size_t i = 1; i < iv.size(); ++i) {
-        if (iv[i].lo < iv[i - 1].hi && iv[i].hi > iv[i].lo && iv[i - 1].hi > iv[i - 1].lo)
-            return fail(AR_ERR_INVALID_ARGUMENT, "%s[%d] overlaps %s[%d] (only the documented in-place layout may alias)",
-                        iv[i].what, iv[i].rank, iv[i - 1].what, iv[i - 1].rank);
-    }
+    size_t a, b;
+    if (find_overlap(iv, &a, &b))
+        return fail(AR_ERR_INVALID_ARGUMENT, "%s[%d] overlaps %s[%d] (only the documented in-place layout may alias)",
+                    iv[a].what, iv[a].rank, iv[b].what, iv[b].rank);
     return AR_SUCCESS;
 }
 
@@ -872,11 +890,10 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
         }
     }
     if (total == 0) return AR_SUCCESS;
-    std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
-    for (size_t i = 1; i < iv.size(); ++i)
-        if (iv[i].lo < iv[i - 1].hi)
-            return fail(AR_ERR_INVALID_ARGUMENT, "%s %d overlaps %s %d (only send == recv may alias)", iv[i].what,
-                        iv[i].rank, iv[i - 1].what, iv[i - 1].rank);
+    size_t oa, ob;
+    if (find_overlap(iv, &oa, &ob))
+        return fail(AR_ERR_INVALID_ARGUMENT, "%s %d overlaps %s %d (only send == recv may alias)", iv[oa].what,
+                    iv[oa].rank, iv[ob].what, iv[ob].rank);
 
     DeviceGuard g(comm->device);
     if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");

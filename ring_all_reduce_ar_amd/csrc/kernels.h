@@ -137,7 +137,8 @@ struct A2AArgs {
 hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream);
 
 // Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
-// has checked alignment and q % (16/elem) == 0); `nt` selects non-temporal
+// has checked that every rank pointer is 16-byte aligned, and for the
+// reduce-scatter layout also q % (16/elem) == 0); `nt` selects non-temporal
 // loads and stores (footprints beyond the last-level cache) over cached ones.
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
                                int grid_x, hipStream_t stream);

@@ -1,8 +1,8 @@
 // kernels_impl.h -- device code of the ring all-reduce for CDNA4 (gfx950):
 // element formats, reduce ops, the kernels, and per-dtype dispatch templates.
 // Each dtype is instantiated in its own translation units (dtype_*.hip,
-// tree_*.hip) so the build compiles them in parallel; kernels.hip holds the dtype switch and the
-// dtype-free copy kernels.
+// tree_*.hip) so the build compiles them in parallel; kernels.hip holds the
+// dtype switch and the dtype-free copy kernels.
 //
 // The reduction is elementwise and HBM-bound: one combine per element and
 // rank against 2*sizeof(T) bytes moved, far below any matrix-core ridge, so
