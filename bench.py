@@ -39,6 +39,7 @@ METRIC = "all-reduce algbw/busbw GB/s and % HBM peak, N=8 ranks, 64 MiB–14 GB 
 HBM_PEAK_GBPS = 8000.0
 LLC_BYTES = 256 << 20      # MI355X last-level (Infinity) cache
 ROTATE_BYTES = 1 << 30    # rotated footprint for calls that fit in it
+COPY_CEILING_BYTES = 1 << 30  # plain copy timed beside every bench line
 CSRC = os.path.join(ROOT, "ring_all_reduce_ar_amd", "csrc")
 
 # workload name -> (nranks, count, dtype, op, description)
@@ -139,29 +140,37 @@ def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "a
             "seconds": dt}
 
 
+def time_copy(torch, ar, nbytes: int, steps: int, warmup: int):
+    """Plain device copy of `nbytes` (a one-rank all-gather: 16-byte loads
+    and stores, src read once, dst written once). Returns (ms per copy,
+    HBM GB/s counting read + write)."""
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    with ar.Comm(1, 0) as comm:
+        def step():
+            ar.ar_all_gather(comm, [src.data_ptr()], [dst.data_ptr()], nbytes // 4, "i32", "fused", stream)
+
+        for _ in range(warmup):
+            step()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    assert torch.equal(src, dst)
+    del src, dst
+    torch.cuda.empty_cache()
+    return ms, 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def copy_probe(args, torch, ar):
     """Plain copy of a known size: src read once, dst written once."""
     nbytes = args.copy_probe
-    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    comm = ar.Comm(1, 0)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        ar.ar_all_gather(comm, [src.data_ptr()], [dst.data_ptr()], nbytes // 4, "i32", "fused", stream)
-
-    for _ in range(args.warmup):
-        step()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    assert torch.equal(src, dst)
-    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    ms, gbps = time_copy(torch, ar, nbytes, args.steps, args.warmup)
     print(json.dumps({"probe": "copy", "bytes": nbytes, "ms_per_copy": round(ms, 4), "hbm_gbps": round(gbps, 1),
                       "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": args.steps}), flush=True)
 
@@ -417,6 +426,12 @@ def main():
         result["cache_resident"] = {"ms_per_step": round(warm_ms, 4),
                                     "effective_gbps": round(alg_bytes / (warm_ms * 1e-3) / 1e9, 1),
                                     "note": "one buffer set called back to back; served from the last-level cache"}
+    # A plain 1 GiB device copy in the same process: the practical ceiling of
+    # a read-once write-once stream on this machine, reported beside the roofline.
+    cms, cgbps = time_copy(torch, ar, COPY_CEILING_BYTES, 20, 3)
+    result["copy_ceiling"] = {"bytes": COPY_CEILING_BYTES, "ms": round(cms, 4), "hbm_gbps": round(cgbps, 1),
+                              "hbm_frac": round(cgbps / HBM_PEAK_GBPS, 4),
+                              "achieved_over_copy": round(achieved / cgbps, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload, coll)
