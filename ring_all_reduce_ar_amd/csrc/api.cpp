@@ -208,14 +208,17 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
 //  - N <= 4: 2 per CU beat 8 by 4-10 points once the data exceeds the
 //    last-level cache; cache-resident calls are within 2 points of each other
 //    and take 8;
-//  - 5 <= N <= 32: 4 per CU is best or within 1 point (the 8 x 14 GB fp16
-//    workload: 75.0% against 74.1% at 8);
+//  - 5 <= N <= 32: up to 128 MiB per rank, 16 per CU (8 ranks x 25 MiB, a
+//    DDP bucket, with cache rotation: 60.2% against 56.5% at 4); above, 4
+//    per CU is best or within 1 point (8 x 14 GB fp16: 75.0% against 74.1%
+//    at 8);
 //  - N > 32: 16 per CU up to 128 MiB per rank, 12 above.
 int fused_per_cu(size_t bytes_per_rank, int nranks, bool cached)
 {
+    const bool small = bytes_per_rank <= (size_t(128) << 20);
     if (nranks <= 4) return cached ? 8 : 2;
-    if (nranks <= 32) return 4;
-    return bytes_per_rank <= (size_t(128) << 20) ? 16 : 12;
+    if (nranks <= 32) return small ? 16 : 4;
+    return small ? 16 : 12;
 }
 
 // Records the start of a call and the end of each step when timing is on.
