@@ -30,7 +30,8 @@ import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-MAX_RANKS = 64
+MAX_RANKS = 64  # AR_MAX_RANKS
+MAX_TENSORS = 65536  # AR_MAX_TENSORS
 
 # ar_result_t
 AR_SUCCESS, AR_ERR_INVALID_ARGUMENT, AR_ERR_UNSUPPORTED, AR_ERR_HIP, AR_ERR_OUT_OF_MEMORY, AR_ERR_INTERNAL = range(6)

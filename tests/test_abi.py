@@ -95,3 +95,10 @@ def test_one_hip_runtime_in_the_process():
     p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert p.returncode == 0, p.stderr
     assert p.stdout.split() == ["1", "1"], p.stdout
+
+
+def test_binding_limits_match_the_header():
+    text = open(HEADER, encoding="utf-8").read()
+    defs = dict(re.findall(r"#define\s+(AR_MAX_\w+)\s+(\d+)", text))
+    assert int(defs["AR_MAX_RANKS"]) == ar.MAX_RANKS
+    assert int(defs["AR_MAX_TENSORS"]) == ar.MAX_TENSORS

@@ -227,3 +227,21 @@ def test_multi_many_launches_and_two_streams():
         torch.cuda.synchronize()
         _check_multi(ra, ea, dtype, "stream 1")
         _check_multi(rb, eb, dtype, "stream 2")
+
+
+def test_multi_at_the_tensor_limit():
+    """AR_MAX_TENSORS tensors per rank (views of 16-element slices of one
+    allocation per rank, in place), then one more is INVALID_ARGUMENT."""
+    n, per, t = 8, 16, ar.MAX_TENSORS
+    count = per * t
+    with ar.Comm(n, 0) as comm:
+        flat = gu.make_inputs(n, count, "f32", "sum", seed=77)
+        exp = oracle.fold_all_reduce([gu.host(x) for x in flat], "f32", "sum")
+        rows = [[flat[r].data_ptr() + k * per * 4 for r in range(n)] for k in range(t)]
+        ar.ar_all_reduce_multi(comm, rows, rows, [per] * t, "f32", "sum")
+        torch.cuda.synchronize()
+        for r in range(n):
+            gu.assert_same(gu.host(flat[r]), exp[r], "f32", f"{t} tensors rank {r}")
+        with pytest.raises(ar.ArError) as ei:
+            ar.ar_all_reduce_multi(comm, rows + rows[:1], rows + rows[:1], [per] * (t + 1), "f32", "sum")
+        assert ei.value.code == ar.AR_ERR_INVALID_ARGUMENT

@@ -85,3 +85,25 @@ def test_special_values_multi_and_scatter(dtype):
             for r in range(n):
                 gu.assert_same(gu.host(recv[r].view), rs_exp[r], dtype, f"rs {dtype} {op} rank {r}")
                 gu.assert_same(gu.host(recv[r].view), exp[r][r * q:(r + 1) * q], dtype, f"rs vs ar rank {r}")
+
+
+@pytest.mark.parametrize("mode", ("fused", "stepwise", "tree"))
+@pytest.mark.parametrize("n", (2, 3, 8))
+def test_int32_wrap_and_truncation(n, mode):
+    """int32 at the type's limits: SUM and PROD wrap modulo 2^32, AVG of the
+    wrapped sum truncates toward zero (negative sums included), MAX/MIN see
+    INT32_MIN and INT32_MAX; against the oracle, bit for bit."""
+    count = n * (4096 + 4) + 3
+    rng = np.random.default_rng(50 + n)
+    edge = np.array([2**31 - 1, -2**31, 2**31 - 2, -2**31 + 1, 0, -1, 1, 2**30, -2**30, 7, -7], dtype=np.int64)
+    with ar.Comm(n, 0) as comm:
+        for op in ("sum", "avg", "max", "min", "prod"):
+            vals = rng.integers(-2**31, 2**31, size=(n, count), dtype=np.int64)
+            pick = rng.random((n, count)) < 0.3
+            vals[pick] = edge[rng.integers(0, edge.size, size=int(pick.sum()))]
+            xs = [torch.from_numpy(vals[r].astype(np.int32)).cuda() for r in range(n)]
+            hosts = [gu.host(x) for x in xs]
+            exp = oracle.tree_all_reduce(hosts, "i32", op) if mode == "tree" else oracle.fold_all_reduce(hosts, "i32", op)
+            outs, _, _ = gu.run_all_reduce(comm, xs, "i32", op, mode)
+            for r in range(n):
+                gu.assert_same(outs[r], exp[r], "i32", f"n={n} i32 {op} {mode} rank {r}")
