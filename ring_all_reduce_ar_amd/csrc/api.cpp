@@ -971,7 +971,7 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
                 if (pc.flags & ar::kPieceVec) {
                     uint64_t vb, ve;
                     ar::piece_vectors(pc.j0, pc.j0 + pc.len, (pc.flags >> ar::kPieceShiftBit) & 7u, E, &vb, &ve);
-                    nt = std::max<uint64_t>(1, ceil_div(ve - vb, ar::kBlock));
+                    nt = std::max<uint64_t>(1, ceil_div(ve - vb, ar::kMultiVecTile));
                 } else {
                     nt = ceil_div(pc.len, ar::kBlock);
                 }

@@ -107,6 +107,9 @@ struct MultiPiece {
 };
 static_assert(sizeof(MultiPiece) == 24, "MultiPiece layout");
 constexpr int kMultiBlobBytes = 3840;
+// Vector pieces are cut into tiles of two kBlock-vector halves (a thread
+// takes one vector in each); element pieces into tiles of kBlock elements.
+constexpr int kMultiVecTile = 2 * kBlock;
 struct MultiHeader {
     int n;
     int npieces;

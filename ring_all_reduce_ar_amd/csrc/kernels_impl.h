@@ -333,6 +333,27 @@ __device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, 
 // Per-row rotation of the fused sweep, in tiles (odd, not a power of two).
 constexpr uint64_t kRowSkewTiles = 37;
 
+// The NR vectors of one element group, loaded in fold order (the chunk's
+// first rank first): combined in that order, finalized, packed.
+template <class F, int OP, int NR>
+__device__ __forceinline__ u32x4 fold_loaded(const u32x4 (&x)[NR])
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    Acc acc[E];
+    F::unpack(x[0], acc);
+#pragma unroll
+    for (int k = 1; k < NR; ++k) {
+        Acc t[E];
+        F::unpack(x[k], t);
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], NR);
+    return F::pack(acc);
+}
+
 // Body of the fused kernel for NR ranks known at compile time: tiles t and
 // t + G (G = gridDim.x) per iteration, rotated by `rot`, with all 2*NR loads
 // issued before either fold (twice the reads in flight per thread; measured
@@ -344,8 +365,6 @@ template <class F, int OP, int NR, bool SCATTER, bool NT>
 __device__ __forceinline__ void fused_x2(const ReduceArgs& a, int c, uint64_t org, uint64_t v0, uint64_t v1,
                                          uint64_t ntiles, uint64_t rot)
 {
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
     const uint64_t G = gridDim.x;
     const void* sp[NR];
 #pragma unroll
@@ -370,18 +389,7 @@ __device__ __forceinline__ void fused_x2(const ReduceArgs& a, int c, uint64_t or
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             if (ok[u]) {
-                Acc acc[E];
-                F::unpack(x[u][0], acc);
-#pragma unroll
-                for (int k = 1; k < NR; ++k) {
-                    Acc t2[E];
-                    F::unpack(x[u][k], t2);
-#pragma unroll
-                    for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t2[j], acc[j]);
-                }
-#pragma unroll
-                for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], NR);
-                const u32x4 out = F::pack(acc);
+                const u32x4 out = fold_loaded<F, OP, NR>(x[u]);
                 if constexpr (SCATTER) {
                     stv<NT>(a.recv[c], vv[u] - v0, out);
                 } else {
@@ -991,15 +999,38 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
             const uint64_t boff = a0 * (16 / E);
             uint64_t vb, ve;
             piece_vectors(pc.j0, j_end, a0, E, &vb, &ve);
-            const uint64_t v = vb + static_cast<uint64_t>(ti) * kBlock + threadIdx.x;
-            if (v < ve) {
-                Acc acc[E];
-                fold_vec<F, OP, NR, NT>(send, c, n, v, acc, boff);
+            // the tile's two halves: vectors v and v + kBlock of this thread
+            const uint64_t v = vb + static_cast<uint64_t>(ti) * kMultiVecTile + threadIdx.x;
+            const bool ok[2] = {v < ve, v + kBlock < ve};
+            if constexpr (NR > 0) {
+                // all 2*NR loads in flight before either fold
+                const void* sp[NR];
 #pragma unroll
-                for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
-                const u32x4 out = F::pack(acc);
+                for (int k = 0; k < NR; ++k) sp[k] = send[wrap_rank(c + k, NR)];
+                u32x4 x[2][NR];
 #pragma unroll
-                for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], v * 16 + boff, out);
+                for (int u = 0; u < 2; ++u)
+                    if (ok[u]) {
+#pragma unroll
+                        for (int k = 0; k < NR; ++k) x[u][k] = ldv_at<NT>(sp[k], (v + u * kBlock) * 16 + boff);
+                    }
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    if (ok[u]) {
+                        const u32x4 out = fold_loaded<F, OP, NR>(x[u]);
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) stv_at<NT>(recv[r], (v + u * kBlock) * 16 + boff, out);
+                    }
+            } else {
+                for (int u = 0; u < 2; ++u) {
+                    if (!ok[u]) continue;
+                    Acc acc[E];
+                    fold_vec<F, OP, NR, NT>(send, c, n, v + u * kBlock, acc, boff);
+#pragma unroll
+                    for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
+                    const u32x4 out = F::pack(acc);
+                    for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], (v + u * kBlock) * 16 + boff, out);
+                }
             }
             if (ti == 0) {
                 // elements before the first whole vector and after the last
