@@ -1,28 +1,39 @@
 """Benchmark of the all-reduce hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grad7b]
-                    [--mode fused|stepwise] [--no-cpu-baseline]
+                    [--mode fused|stepwise|graph|tree|tree_stepwise]
+                    [--collective all_reduce|reduce_scatter|all_gather|all_to_all]
+                    [--multi] [--no-cpu-baseline]
+    python bench.py --sweep            # 1 KiB..256 MiB per rank, every mode, alpha-beta fit
+    python bench.py --copy-probe BYTES # a plain device copy (HBM counter calibration)
 
-One "step" is one in-place all-reduce of the whole workload: every virtual
-rank's buffer (inputs already resident in HBM) reduced and the result
+One "step" is one call of the collective on the whole workload: every
+virtual rank's buffer (inputs already resident in HBM) reduced and the result
 written back to every rank. The default workload is the 7e9-element fp16
 gradient per rank (14 GB, the 7B model of the geek-doc page "训练梯度同步与
 集合通信", sections 一 and 四) at 8 virtual ranks, AVG with fp32
-accumulation, fused mode.
+accumulation, fused mode, in place. The rank buffers are allocated and timed
+twice; the second pass is reported (the first as
+first_allocation_ms_per_step). Calls whose rank buffers fit in the
+last-level cache rotate buffer sets so every timed call reads HBM.
 
 Reported (one JSON line):
   value        algbw = S / T, S = bytes per rank (handbook "集合通信原语",
                section 算法带宽与总线带宽)
-  busbw        algbw * 2(N-1)/N (same section)
-  roofline     the fused kernel's algorithmic HBM bytes 2*N*S per launch
-               (each rank's input read once, N outputs written once) over its
-               average launch time, against the 8 TB/s HBM peak; traffic =
-               bytes the HBM counters saw per launch (rocprofv3 FETCH_SIZE +
-               WRITE_SIZE, scaled by a plain copy's reading), from the
-               committed profile when it matches the current kernel source,
-               else null
-  cpu_baseline the CPU oracle (the literal ring, one thread) on a window of
-               the same workload, in the same unit
+  busbw        algbw * 2(N-1)/N for all-reduce, (N-1)/N for the others
+               (same section)
+  step_ms      median / min / max of the single timed steps
+  roofline     the call's algorithmic HBM bytes (all-reduce and all-to-all
+               2*N*S, reduce-scatter and all-gather (N+1)*S) over its time,
+               against the 8 TB/s HBM peak; traffic = bytes the HBM counters
+               saw per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+               plain copy's reading), from the committed profile when it
+               matches the current kernel source, else null
+  copy_ceiling a plain 1 GiB device copy timed in the same process: the
+               practical read-once write-once rate of this machine, and the
+               call's rate over it
+  cpu_baseline the CPU oracle (one thread) on a window of the same workload,
+               in the same unit
 """
 from __future__ import annotations
 
