@@ -61,7 +61,7 @@ typedef struct ar_comm* ar_comm_t;
 typedef enum {
     AR_SUCCESS = 0,
     AR_ERR_INVALID_ARGUMENT = 1, /* bad pointer, enum, size, alias or workspace */
-    AR_ERR_UNSUPPORTED = 2,      /* a valid request this build does not serve */
+    AR_ERR_UNSUPPORTED = 2,      /* a valid request the library does not serve */
     AR_ERR_HIP = 3,              /* a HIP runtime call or kernel launch failed */
     AR_ERR_OUT_OF_MEMORY = 4,    /* host allocation for the comm failed */
     AR_ERR_INTERNAL = 5
