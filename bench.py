@@ -22,7 +22,9 @@ Reported (one JSON line):
                section 算法带宽与总线带宽)
   busbw        algbw * 2(N-1)/N for all-reduce, (N-1)/N for the others
                (same section)
-  step_ms      median / min / max of the single timed steps
+  ms_per_step  the K timed steps between two events, over K
+  step_ms      median / min / max of single steps, from a second pass of K
+               steps with an event after each
   roofline     the call's algorithmic HBM bytes (all-reduce and all-to-all
                2*N*S, reduce-scatter and all-gather (N+1)*S) over its time,
                against the 8 TB/s HBM peak; traffic = bytes the HBM counters
@@ -320,7 +322,8 @@ def main():
 
     def timed_pass(measure_warm: bool):
         """Allocate and fill the rank buffers, warm up, time exactly K steps
-        (an event after each step gives the per-step times)."""
+        between two events; then K more steps with an event after each for
+        the per-step times."""
         print(f"[bench] generating {desc}" + (f" ({sets} rotating buffer sets)" if sets > 1 else ""),
               file=sys.stderr, flush=True)
         # the input side: count elements per rank, or count/N for all-gather
@@ -362,22 +365,31 @@ def main():
                 rows = rowsets[i % sets]
                 ar.ar_all_reduce_multi(comm, rows, rows, sizes, dtype, op, "fused", stream)
 
-        def run(k, rotate):
+        def run(k, rotate, per_step_events=False):
+            # The timed pass brackets the K steps with two events only: an
+            # event recorded between kernels costs the stream a few
+            # microseconds, which shows at short calls. The per-step times
+            # come from a separate pass with an event after every step.
             for i in range(args.warmup):
                 step(i if rotate else 0)
             torch.cuda.synchronize()
-            events = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+            events = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1 if per_step_events else 2)]
             torch.cuda.synchronize()
             events[0].record(stream)
             for i in range(k):
                 step(i if rotate else 0)
-                events[i + 1].record(stream)
+                if per_step_events:
+                    events[i + 1].record(stream)
+            if not per_step_events:
+                events[1].record(stream)
             torch.cuda.synchronize()
-            per_step = [events[i].elapsed_time(events[i + 1]) for i in range(k)]
-            return events[0].elapsed_time(events[k]) / k, per_step
+            if not per_step_events:
+                return events[0].elapsed_time(events[1]) / k, None
+            return None, [events[i].elapsed_time(events[i + 1]) for i in range(k)]
 
         print(f"[bench] timing {args.warmup} warmup + {args.steps} steps", file=sys.stderr, flush=True)
-        ms_, per_step = run(args.steps, True)
+        ms_ = run(args.steps, True)[0]
+        per_step = run(args.steps, True, per_step_events=True)[1]
         warm = run(args.steps, False)[0] if measure_warm and sets > 1 else None
         ar.ar_comm_set_workspace(comm, None)
         del bufsets, ptrsets, outsets, outptrs, ws
