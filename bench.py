@@ -34,7 +34,7 @@ Reported (one JSON line):
   copy_ceiling a plain 1 GiB device copy timed in the same process: the
                practical read-once write-once rate of this machine, and the
                call's rate over it
-  cpu_baseline the CPU oracle (one thread) on a window of the same workload,
+  cpu_baseline the CPU oracle (one thread) on the workload, or a window of it,
                in the same unit
 """
 from __future__ import annotations
@@ -72,6 +72,7 @@ WORKLOADS = {
 }
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4}
 CPU_WINDOW_LOG2 = 27  # elements per rank in the CPU oracle's window (about 10 s of oracle work)
+CPU_MIN_SECONDS = 5.0  # a shorter sample is repeated until this much oracle time has passed
 
 
 def alpha_beta_time(nranks: int, msg_bytes: float, alpha_s: float, beta_bytes_per_s: float):
@@ -118,38 +119,50 @@ def load_traffic(workload: str, mode: str):
     return float(t.group(1))
 
 
-def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "all_reduce"):
-    """The oracle on a window of the same workload (2^CPU_WINDOW_LOG2
-    elements per rank on the large side, seeded the same way), timed on one
-    host thread: the literal ring for all-reduce, the oracle's reduce-scatter,
-    all-gather or all-to-all otherwise. algbw convention as the GPU line."""
+def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "all_reduce", count: int = 0):
+    """The oracle on a sample of the same workload, timed on one host
+    thread: the literal ring for all-reduce, the oracle's reduce-scatter,
+    all-gather or all-to-all otherwise. The sample is the workload itself
+    when its `count` elements per rank fit in 2^CPU_WINDOW_LOG2, else a
+    window of that many elements per rank, seeded the same way; a sample
+    that runs in under CPU_MIN_SECONDS is repeated until that much time has
+    passed. algbw convention as the GPU line."""
     import oracle
     import synthetic
-    count = 1 << CPU_WINDOW_LOG2
+    window = 1 << CPU_WINDOW_LOG2
+    sample = min(count, window) if count > 0 else window
     wl = workload if workload in synthetic.WORKLOAD_IDS else "sweep"
-    in_count = count // nranks if coll == "all_gather" else count
+    in_count = sample // nranks if coll == "all_gather" else sample
     # generated on the device (fast), copied to host memory before timing
     import torch
     dev = "cuda" if torch.cuda.is_available() else "cpu"
     xs = [synthetic.to_numpy(t) for t in synthetic.rank_inputs(wl, nranks, in_count, dtype, device=dev, op=op)]
+    what = {"all_reduce": "literal ring (N-1 reduce-scatter + N-1 all-gather steps)", "reduce_scatter": "reduce-scatter",
+            "all_gather": "all-gather"}.get(coll, "all-to-all")
+
+    def once():
+        if coll == "all_reduce":
+            oracle.ring_all_reduce(xs, dtype, op)
+        elif coll == "reduce_scatter":
+            oracle.reduce_scatter(xs, dtype, op)
+        elif coll == "all_gather":
+            oracle.all_gather(xs, dtype)
+        else:
+            oracle.all_to_all(xs, dtype)
+
+    reps = 0
     t0 = time.perf_counter()
-    if coll == "all_reduce":
-        oracle.ring_all_reduce(xs, dtype, op)
-        what = "literal ring (N-1 reduce-scatter + N-1 all-gather steps)"
-    elif coll == "reduce_scatter":
-        oracle.reduce_scatter(xs, dtype, op)
-        what = "reduce-scatter"
-    elif coll == "all_gather":
-        oracle.all_gather(xs, dtype)
-        what = "all-gather"
-    else:
-        oracle.all_to_all(xs, dtype)
-        what = "all-to-all"
-    dt = time.perf_counter() - t0
-    s_bytes = count * ESIZE[dtype]
-    return {"value": s_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nranks} ranks x 2^{CPU_WINDOW_LOG2} {dtype} elements per rank ({s_bytes / 2**20:.0f} MiB), "
-                      f"{what}, {op}, single thread",
+    while True:
+        once()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_MIN_SECONDS:
+            break
+    s_bytes = sample * ESIZE[dtype]
+    part = "the whole workload" if sample == count else f"a window of the {count}-element workload" if count else "a window"
+    return {"value": s_bytes * reps / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nranks} ranks x {sample} {dtype} elements per rank ({s_bytes / 2**20:.1f} MiB; {part}), "
+                      f"{what}, {op}, single thread" + (f", {reps} calls" if reps > 1 else ""),
             "seconds": dt}
 
 
@@ -457,7 +470,7 @@ def main():
                               "achieved_over_copy": round(achieved / cgbps, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload, coll)
+        result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload, coll, count)
     print(json.dumps(result), flush=True)
 
 
