@@ -1,0 +1,31 @@
+"""Host-side logic of bench.py's CPU baseline: which sample of the workload the
+oracle is timed on, and how a short sample is repeated."""
+import bench
+
+
+def test_cpu_baseline_takes_the_whole_workload_when_it_fits(monkeypatch):
+    monkeypatch.setattr(bench, "CPU_MIN_SECONDS", 0.0)
+    r = bench.cpu_baseline(4, "f32", "sum", "sweep", "all_reduce", count=4096)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s"
+    assert "4 ranks x 4096 f32 elements per rank" in r["sample"]
+    assert "the whole workload" in r["sample"]
+    assert r["value"] > 0 and r["seconds"] > 0
+
+
+def test_cpu_baseline_windows_a_larger_workload(monkeypatch):
+    monkeypatch.setattr(bench, "CPU_MIN_SECONDS", 0.0)
+    monkeypatch.setattr(bench, "CPU_WINDOW_LOG2", 10)
+    r = bench.cpu_baseline(8, "f16", "avg", "grad7b", "reduce_scatter", count=7_000_000_000)
+    assert "8 ranks x 1024 f16 elements per rank" in r["sample"]
+    assert "a window of the 7000000000-element workload" in r["sample"]
+    assert "reduce-scatter" in r["sample"]
+
+
+def test_cpu_baseline_repeats_a_short_sample(monkeypatch):
+    monkeypatch.setattr(bench, "CPU_MIN_SECONDS", 0.05)
+    r = bench.cpu_baseline(2, "i32", "sum", "sweep", "all_gather", count=64)
+    assert r["seconds"] >= 0.05
+    assert r["sample"].endswith(" calls")
+    calls = int(r["sample"].rsplit(", ", 1)[1].split()[0])
+    # the rate counts every call: bytes per call x calls / time
+    assert abs(r["value"] - 64 * 4 * calls / r["seconds"] / 1e9) <= 1e-9 * r["value"] + 1e-12
