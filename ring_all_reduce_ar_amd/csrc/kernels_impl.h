@@ -270,64 +270,48 @@ __device__ __forceinline__ typename F::Acc fold_elem(const void* const* send, in
     return acc;
 }
 
-// Vector vi (16 bytes) of chunk c, all ranks, in ring order. NR > 0 fixes the
-// rank count at compile time (all NR loads issued before the first combine);
-// NR == 0 takes it from the arguments and loads in batches of 8.
-// The 16 bytes at byte offset `off` of NR buffers already listed in fold
-// order (the chunk's first rank first): all NR loads are issued, then
-// combined in that order.
-template <class F, int OP, int NR, bool NT>
-__device__ __forceinline__ void fold_vec_ordered(const void* const (&sp)[NR], uint64_t off, typename F::Acc* acc)
+// Two 16-byte vectors of every rank, at byte offsets off[0] and off[1] past
+// the rank pointers (ok[u] says which exist), folded in ring order from rank
+// c and finalized into out[0] and out[1], for a rank count n known only at
+// run time. The ranks go in batches of 8; each batch issues its loads for
+// both vectors (16 in flight per thread) before combining them in order
+// (measured 3-5% faster than one vector at a time at 16-64 ranks).
+template <class F, int OP, bool NT>
+__device__ __forceinline__ void fold_pair_any(const void* const* send, int c, int n, const uint64_t (&off)[2],
+                                              const bool (&ok)[2], u32x4 (&out)[2])
 {
     using Acc = typename F::Acc;
     constexpr int E = F::kEpv;
-    u32x4 x[NR];
+    Acc acc[2][E];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) x[k] = ldv_at<NT>(sp[k], off);
-    F::unpack(x[0], acc);
+    for (int u = 0; u < 2; ++u)
+        if (ok[u]) F::unpack(ldv_at<NT>(send[c], off[u]), acc[u]);
+    for (int k = 1; k < n; k += 8) {
+        const int b = min(8, n - k);
+        u32x4 x[2][8];
 #pragma unroll
-    for (int k = 1; k < NR; ++k) {
-        Acc t[E];
-        F::unpack(x[k], t);
-#pragma unroll
-        for (int j = 0; j < E; ++j) acc[j] = combine<OP>(t[j], acc[j]);
-    }
-}
-
-// Vector vi of every rank, `boff` bytes past the rank pointers (0 unless the
-// vectors start past an unaligned base); the offset is one per-thread value,
-// so the rank pointers stay plain bases.
-template <class F, int OP, int NR, bool NT>
-__device__ __forceinline__ void fold_vec(const void* const* send, int c, int n, uint64_t vi, typename F::Acc* acc,
-                                         uint64_t boff = 0)
-{
-    using Acc = typename F::Acc;
-    constexpr int E = F::kEpv;
-    const uint64_t off = vi * 16 + boff;
-    if constexpr (NR > 0) {
-        const void* sp[NR];
-#pragma unroll
-        for (int k = 0; k < NR; ++k) sp[k] = send[wrap_rank(c + k, NR)];
-        fold_vec_ordered<F, OP, NR, NT>(sp, off, acc);
-    } else {
-        F::unpack(ldv_at<NT>(send[c], off), acc);
-        for (int k = 1; k < n; k += 8) {
-            const int b = min(8, n - k);
-            u32x4 x[8];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (j < b) x[j] = ldv_at<NT>(send[wrap_rank(c + k + j, n)], off);
+                if (ok[u] && j < b) x[u][j] = ldv_at<NT>(send[wrap_rank(c + k + j, n)], off[u]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < b) {
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (ok[u] && j < b) {
                     Acc t[E];
-                    F::unpack(x[j], t);
+                    F::unpack(x[u][j], t);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] = combine<OP>(t[e], acc[e]);
+                    for (int e = 0; e < E; ++e) acc[u][e] = combine<OP>(t[e], acc[u][e]);
                 }
-            }
-        }
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        if (ok[u]) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) acc[u][j] = finalize<OP>(acc[u][j], n);
+            out[u] = F::pack(acc[u]);
+        }
 }
 
 // Per-row rotation of the fused sweep, in tiles (odd, not a power of two).
@@ -433,20 +417,30 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     if constexpr (NR > 0) {
         fused_x2<F, OP, NR, SCATTER, NT>(a, c, org, v0, v1, ntiles, rot);
     } else {
-        for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-            const uint64_t tr = t + rot < ntiles ? t + rot : t + rot - ntiles;
-            const uint64_t v = org + tr * kBlock + threadIdx.x;
-            if (v < v0 || v >= v1) continue;
-            Acc acc[E];
-            fold_vec<F, OP, NR, NT>(a.send, c, n, v, acc);
+        // tiles t and t + G per iteration, as fused_x2 does
+        const uint64_t G = gridDim.x;
+        for (uint64_t t = blockIdx.x; t < ntiles; t += 2 * G) {
+            uint64_t vv[2], off[2];
+            bool ok[2];
 #pragma unroll
-            for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
-            const u32x4 out = F::pack(acc);
-            if constexpr (SCATTER) {
-                stv<NT>(a.recv[c], v - v0, out);
-            } else {
-                for (int r = 0; r < n; ++r) stv<NT>(a.recv[r], v, out);
+            for (int u = 0; u < 2; ++u) {
+                const uint64_t tu = t + u * G;
+                const uint64_t tr = tu + rot < ntiles ? tu + rot : tu + rot - ntiles;
+                vv[u] = org + tr * kBlock + threadIdx.x;
+                off[u] = vv[u] * 16;
+                ok[u] = tu < ntiles && vv[u] >= v0 && vv[u] < v1;
             }
+            u32x4 out[2];
+            fold_pair_any<F, OP, NT>(a.send, c, n, off, ok, out);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (ok[u]) {
+                    if constexpr (SCATTER) {
+                        stv<NT>(a.recv[c], vv[u] - v0, out[u]);
+                    } else {
+                        for (int r = 0; r < n; ++r) stv<NT>(a.recv[r], vv[u], out[u]);
+                    }
+                }
         }
     }
     // Head [lo, v0 E) and tail [v1 E, hi): fewer than E elements each.
@@ -1022,15 +1016,13 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
                         for (int r = 0; r < NR; ++r) stv_at<NT>(recv[r], (v + u * kBlock) * 16 + boff, out);
                     }
             } else {
-                for (int u = 0; u < 2; ++u) {
-                    if (!ok[u]) continue;
-                    Acc acc[E];
-                    fold_vec<F, OP, NR, NT>(send, c, n, v + u * kBlock, acc, boff);
+                const uint64_t off[2] = {v * 16 + boff, (v + kBlock) * 16 + boff};
+                u32x4 out[2];
+                fold_pair_any<F, OP, NT>(send, c, n, off, ok, out);
 #pragma unroll
-                    for (int j = 0; j < E; ++j) acc[j] = finalize<OP>(acc[j], n);
-                    const u32x4 out = F::pack(acc);
-                    for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], (v + u * kBlock) * 16 + boff, out);
-                }
+                for (int u = 0; u < 2; ++u)
+                    if (ok[u])
+                        for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], off[u], out[u]);
             }
             if (ti == 0) {
                 // elements before the first whole vector and after the last
