@@ -28,9 +28,13 @@ Reported (one JSON line):
   roofline     the call's algorithmic HBM bytes (all-reduce and all-to-all
                2*N*S, reduce-scatter and all-gather (N+1)*S) over its time,
                against the 8 TB/s HBM peak; traffic = bytes the HBM counters
-               saw per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
-               plain copy's reading), from the committed profile when it
-               matches the current kernel source, else null
+               saw per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+               plain copy's reading; one launch in fused mode, the sum of the
+               2(N-1) launches in stepwise mode), from the committed profile
+               when it matches the current kernel source, else null
+  moved        stepwise and graph modes: the bytes the ring's steps move
+               (5(N-1)*S for fp32/int32, (14N-18)*count with the fp32
+               workspace of fp16/bf16) and their rate
   copy_ceiling a plain 1 GiB device copy timed in the same process: the
                practical read-once write-once rate of this machine, and the
                call's rate over it
@@ -83,6 +87,24 @@ def alpha_beta_time(nranks: int, msg_bytes: float, alpha_s: float, beta_bytes_pe
     lat = 2 * (nranks - 1) * alpha_s
     bw = 2 * (nranks - 1) / nranks * msg_bytes / beta_bytes_per_s
     return lat, bw, lat + bw
+
+
+def ring_moved_bytes(nranks: int, count: int, dtype: str) -> int:
+    """HBM bytes one stepwise ring all-reduce moves, summed over its 2(N-1)
+    launches (the ring of the geek-doc page "训练梯度同步与集合通信", section
+    三). Every step touches each element once, at one rank or another.
+    fp32/int32 partials travel in the rank buffers: a reduce-scatter step
+    reads 2e and writes e bytes per element, an all-gather step reads e and
+    writes e, so 5(N-1)*count*e in all. fp16/bf16 partials stay in an fp32
+    workspace: the first reduce-scatter step reads 2+2 and writes 4 bytes,
+    a middle step reads 2+4 and writes 4, the last reads 2+4 and writes 2
+    (at N = 2 the one step reads 2+2 and writes 2), and an all-gather step
+    reads 2 and writes 2: (14N-18)*count in all."""
+    if nranks < 2:
+        return 0
+    if dtype in ("f16", "bf16"):
+        return (14 * nranks - 18) * count
+    return 5 * (nranks - 1) * count * ESIZE[dtype]
 
 
 def fit_line(xs, ys):
@@ -457,6 +479,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
     }
+    if coll == "all_reduce" and args.mode in ("stepwise", "graph"):
+        moved = ring_moved_bytes(n, count, dtype)
+        result["moved"] = {"bytes": moved, "gbps": round(moved / (ms * 1e-3) / 1e9, 1),
+                           "frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "note": "bytes the 2(N-1) ring steps read and write, over the call's time"}
     if sets > 1:
         result["config"]["rotating_buffer_sets"] = sets
         result["cache_resident"] = {"ms_per_step": round(warm_ms, 4),

@@ -29,3 +29,31 @@ def test_cpu_baseline_repeats_a_short_sample(monkeypatch):
     calls = int(r["sample"].rsplit(", ", 1)[1].split()[0])
     # the rate counts every call: bytes per call x calls / time
     assert abs(r["value"] - 64 * 4 * calls / r["seconds"] / 1e9) <= 1e-9 * r["value"] + 1e-12
+
+
+def _moved_by_steps(n, count, dtype):
+    # walk the ring's steps and add up what each one reads and writes per element
+    e = bench.ESIZE[dtype]
+    half = dtype in ("f16", "bf16")
+    total = 0
+    for s in range(n - 1):  # reduce-scatter
+        first, last = s == 0, s == n - 2
+        if not half:
+            total += 3 * e * count  # local + incoming read, partial written
+        else:
+            incoming = 2 if first else 4  # a neighbour's fp16 input, else its fp32 partial
+            written = 2 if last else 4  # the fp16 result, else an fp32 partial
+            total += (2 + incoming + written) * count
+    total += (n - 1) * 2 * e * count  # all-gather copies
+    return total
+
+
+def test_ring_moved_bytes_matches_the_step_walk():
+    for n in range(2, 10):
+        for dtype in ("f32", "i32", "f16", "bf16"):
+            for count in (1, 7, 4096, 1000003):
+                assert bench.ring_moved_bytes(n, count, dtype) == _moved_by_steps(n, count, dtype), (n, dtype, count)
+    # the figures quoted for 8 ranks: 35*S for fp32, 94*count with the fp32 workspace
+    assert bench.ring_moved_bytes(8, 100, "f32") == 35 * 400
+    assert bench.ring_moved_bytes(8, 100, "f16") == 94 * 100
+    assert bench.ring_moved_bytes(1, 100, "f32") == 0
