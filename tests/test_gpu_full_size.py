@@ -194,3 +194,35 @@ def test_odd_rank_counts_large(n, count, dtype):
         check_sampled(comm, bufs, dtype, "sum", "fused", seed=n)
         del bufs
     free()
+
+
+def _generic_case(n, dtype, extra):
+    # chunk length giving each chunk row 2G + G/3 + 1 tiles of 4 KiB, G being
+    # the row's workgroups at 16 per CU (the 5..64-rank rule up to 128 MiB
+    # per rank), plus `extra` elements so chunks start inside a vector
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = max(1, cus * 16 // n)
+    tiles = 2 * g + g // 3 + 1
+    q = tiles * 256 * gu.EPV[dtype] + extra
+    return n * q - extra // 2
+
+
+@pytest.mark.parametrize("n,dtype,op,extra", [(17, "f32", "sum", 1), (33, "bf16", "avg", 3), (64, "f32", "prod", 1),
+                                              (64, "f16", "max", 5), (12, "i32", "sum", 0)])
+def test_generic_rank_counts_full_compare(n, dtype, op, extra):
+    """Rank counts above 8 take the kernel whose rank count is a run-time
+    value; it folds two tiles per grid-stride iteration. These sizes give
+    every chunk row one iteration in which each workgroup holds two tiles and
+    a second in which only some hold a first tile and none a second, with
+    ragged chunks:
+    every element of every rank against the oracle, out of place, with guard
+    bands."""
+    count = _generic_case(n, dtype, extra)
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=n)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "fused")
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} rank {r}")
+        del xs, exp, got, send, recv
+    free()

@@ -98,6 +98,20 @@ def test_multi_many_tensors_many_launches():
         check(comm, [int(x) for x in rng.integers(1, 2000, size=40)], "bf16", "avg", seed=2)
 
 
+@pytest.mark.parametrize("n", [17, 64])
+def test_multi_generic_rank_count_both_tile_halves(n):
+    """Above 8 ranks the rank count is a run-time value; a multi-tensor tile is
+    two 256-vector halves folded together. Tensors large enough that each
+    chunk holds pieces spanning several tiles, with ragged and shifted
+    pieces, against the oracle and the flat call."""
+    for dtype, op in (("f32", "sum"), ("bf16", "avg"), ("f32", "max")):
+        epv = gu.EPV[dtype]
+        sizes = [3, n * 3 * 256 * epv + 5, 7, n * 2 * 256 * epv - 1, n * 700 + 1]
+        with ar.Comm(n, 0) as comm:
+            check(comm, sizes, dtype, op, seed=n)
+            check(comm, sizes, dtype, op, seed=n + 1, inplace=True)
+
+
 def test_multi_single_tensor_spanning_all_chunks():
     with ar.Comm(8, 0) as comm:
         check(comm, [8 * 50000 + 7], "f16", "sum", seed=4)
