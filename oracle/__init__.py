@@ -40,8 +40,10 @@ GCC_CMD = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle with gcc (always recompiles). Returns the library path."""
-    tmp = out + ".tmp"
+    """Compile the oracle with gcc (always recompiles). Returns the library path.
+    Each process compiles to its own temporary file and renames it into place,
+    so parallel test workers building at once do not race."""
+    tmp = f"{out}.tmp{os.getpid():x}"
     cmd = [tmp if a == _LIB else src if a == _SRC else a for a in GCC_CMD]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)

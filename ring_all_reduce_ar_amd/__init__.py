@@ -130,8 +130,22 @@ def _addr(buf) -> int:
     raise TypeError(f"expected a tensor or an int address, got {type(buf).__name__}")
 
 
+_PTR_ARRAY_TYPES = {}  # length -> ctypes array type (building the type costs more than the array)
+
+
 def _ptrs(bufs):
-    return (ctypes.c_void_p * len(bufs))(*[_addr(b) for b in bufs])
+    n = len(bufs)
+    t = _PTR_ARRAY_TYPES.get(n)
+    if t is None:
+        t = _PTR_ARRAY_TYPES[n] = ctypes.c_void_p * n
+    return t(*[b if type(b) is int else _addr(b) for b in bufs])
+
+
+def _ptr_pair(sendbufs, recvbufs):
+    """The send and recv pointer arrays; one array serves both when the same
+    list is passed for both (in place)."""
+    s = _ptrs(sendbufs)
+    return s, (s if recvbufs is sendbufs else _ptrs(recvbufs))
 
 
 def _stream(stream, device: int):
@@ -206,26 +220,26 @@ def ar_comm_set_workspace(comm, buf, nbytes: int | None = None):
 
 
 def ar_all_reduce(comm, sendbufs, recvbufs, count: int, dtype, op, mode="fused", stream=None):
-    _check(_lib.ar_all_reduce(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), count, _enum(dtype, DTYPE_NAMES, "dtype"),
+    _check(_lib.ar_all_reduce(_h(comm), *_ptr_pair(sendbufs, recvbufs), count, _enum(dtype, DTYPE_NAMES, "dtype"),
                               _enum(op, OP_NAMES, "op"), _enum(mode, MODE_NAMES, "mode"),
                               _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_reduce")
 
 
 def ar_reduce_scatter(comm, sendbufs, recvbufs, recvcount: int, dtype, op, mode="fused", stream=None):
-    _check(_lib.ar_reduce_scatter(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), recvcount,
+    _check(_lib.ar_reduce_scatter(_h(comm), *_ptr_pair(sendbufs, recvbufs), recvcount,
                                   _enum(dtype, DTYPE_NAMES, "dtype"), _enum(op, OP_NAMES, "op"),
                                   _enum(mode, MODE_NAMES, "mode"),
                                   _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_reduce_scatter")
 
 
 def ar_all_gather(comm, sendbufs, recvbufs, sendcount: int, dtype, mode="fused", stream=None):
-    _check(_lib.ar_all_gather(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), sendcount,
+    _check(_lib.ar_all_gather(_h(comm), *_ptr_pair(sendbufs, recvbufs), sendcount,
                               _enum(dtype, DTYPE_NAMES, "dtype"), _enum(mode, MODE_NAMES, "mode"),
                               _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_gather")
 
 
 def ar_all_to_all(comm, sendbufs, recvbufs, blockcount: int, dtype, mode="fused", stream=None):
-    _check(_lib.ar_all_to_all(_h(comm), _ptrs(sendbufs), _ptrs(recvbufs), blockcount,
+    _check(_lib.ar_all_to_all(_h(comm), *_ptr_pair(sendbufs, recvbufs), blockcount,
                               _enum(dtype, DTYPE_NAMES, "dtype"), _enum(mode, MODE_NAMES, "mode"),
                               _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_to_all")
 
@@ -237,7 +251,7 @@ def ar_all_reduce_multi(comm, sendbufs, recvbufs, counts, dtype, op, mode="fused
     flat_s = [b for row in sendbufs for b in row] if nt and isinstance(sendbufs[0], (list, tuple)) else list(sendbufs)
     flat_r = [b for row in recvbufs for b in row] if nt and isinstance(recvbufs[0], (list, tuple)) else list(recvbufs)
     arr = (ctypes.c_size_t * max(nt, 1))(*counts)
-    _check(_lib.ar_all_reduce_multi(_h(comm), nt, _ptrs(flat_s), _ptrs(flat_r), arr, _enum(dtype, DTYPE_NAMES, "dtype"),
+    _check(_lib.ar_all_reduce_multi(_h(comm), nt, *_ptr_pair(flat_s, flat_r), arr, _enum(dtype, DTYPE_NAMES, "dtype"),
                                     _enum(op, OP_NAMES, "op"), _enum(mode, MODE_NAMES, "mode"),
                                     _stream(stream, comm.device if isinstance(comm, Comm) else 0)),
            "ar_all_reduce_multi")

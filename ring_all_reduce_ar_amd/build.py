@@ -73,7 +73,7 @@ def build(verbose: bool = False, jobs: int = 0, incremental: bool = False) -> st
             failed.append(src)
     if failed:
         raise subprocess.CalledProcessError(1, f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = f"{LIB}.tmp{os.getpid():x}"  # per-process name: concurrent builds rename atomically
     subprocess.run(hipcc_link(objs, tmp), check=True)
     os.replace(tmp, LIB)
     return LIB
