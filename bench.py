@@ -116,6 +116,25 @@ def fit_line(xs, ys):
     return my - b * mx, b
 
 
+SWEEP_LATENCY_MAX = 1 << 20  # bytes per rank: the latency regime of the sweep
+
+
+def alpha_beta_fit(points, launches: int, nranks: int):
+    """The alpha-beta model T = launches*alpha + moved/beta fitted in the two
+    regimes where each term shows: alpha from the intercept of a line through
+    the calls of at most SWEEP_LATENCY_MAX bytes per rank, beta from the
+    slope of a line through the calls whose in-place footprint N*S exceeds
+    the last-level cache (HBM-bound). Sizes in between run from that cache
+    and would pull a single line's slope up and its intercept down.
+    points: (bytes per rank, moved bytes, seconds). Returns (alpha seconds
+    per launch, beta bytes per second or None)."""
+    lat = [(m, t) for s, m, t in points if s <= SWEEP_LATENCY_MAX]
+    hbm = [(m, t) for s, m, t in points if nranks * s > LLC_BYTES]
+    a, _ = fit_line(*zip(*lat))
+    b = fit_line(*zip(*hbm))[1] if len(hbm) >= 2 else 0.0
+    return a / launches, (1.0 / b if b > 0 else None)
+
+
 def kernel_sha() -> str:
     """Hash of every kernel source and of the launch code (grid shapes):
     counters taken on other sources are not reported."""
@@ -226,7 +245,8 @@ def copy_probe(args, torch, ar):
 def sweep(args, torch, ar, synthetic):
     """The alpha vs beta regimes: 8 ranks, 1 KiB .. 256 MiB per rank in powers
     of two, fp32 SUM, in place, each mode. One JSON line per (mode, size),
-    then one line with the least-squares fits
+    then one line with the alpha-beta fits (alpha_beta_fit: alpha from the
+    latency regime, beta from the HBM-bound sizes)
       ring modes: T = 2(N-1)*alpha + moved/beta, moved = 5(N-1)*S (the bytes
                   the N-1 reduce-scatter and N-1 all-gather steps move)
       fused:      T = alpha + 2*N*S/beta."""
@@ -274,10 +294,13 @@ def sweep(args, torch, ar, synthetic):
     levels = (n - 1).bit_length()
     for mode in ("fused", "stepwise", "graph", "tree", "tree_stepwise"):
         rs = [r for r in rows if r["sweep"] == mode]
-        a, b = fit_line([r["moved_bytes"] for r in rs], [r["us"] * 1e-6 for r in rs])
         launches = {"fused": 1, "tree": 1, "tree_stepwise": 2 * levels}.get(mode, 2 * (n - 1))
-        fits[mode] = {"alpha_us": round(a / launches * 1e6, 3), "beta_gbps": round(1 / b / 1e9, 1) if b > 0 else None,
-                      "model": "T = %d*alpha + moved/beta" % launches}
+        alpha, beta = alpha_beta_fit([(r["bytes_per_rank"], r["moved_bytes"], r["us"] * 1e-6) for r in rs],
+                                     launches, n)
+        fits[mode] = {"alpha_us": round(alpha * 1e6, 3), "beta_gbps": round(beta / 1e9, 1) if beta else None,
+                      "model": "T = %d*alpha + moved/beta" % launches,
+                      "alpha_from": "sizes up to %d bytes per rank" % SWEEP_LATENCY_MAX,
+                      "beta_from": "sizes with N*S above the %d MiB last-level cache" % (LLC_BYTES >> 20)}
     small = {m: min(r["us"] for r in rows if r["sweep"] == m)
              for m in ("fused", "stepwise", "graph", "tree", "tree_stepwise")}
     print(json.dumps({"sweep_fit": fits, "smallest_call_us": small, "nranks": n, "dtype": "f32", "op": "sum"}),

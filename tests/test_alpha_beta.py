@@ -36,3 +36,21 @@ def test_geek_doc_7b_example():
 def test_fit_line_recovers_a_line():
     a, b = bench.fit_line([1.0, 2.0, 3.0, 10.0], [5.0 + 2 * x for x in (1.0, 2.0, 3.0, 10.0)])
     assert a == pytest.approx(5.0) and b == pytest.approx(2.0)
+
+
+def test_two_regime_fit_recovers_alpha_and_beta():
+    """Calls follow T = L*alpha + moved/beta where the model holds (small
+    calls; calls larger than the last-level cache) and run twice as fast in
+    between, as cache-resident calls do: the fit still returns alpha and
+    beta, where one line through every size would not."""
+    n, launches, alpha, beta = 8, 14, 3e-6, 5e12
+    pts = []
+    for k in range(10, 29):
+        s = 1 << k
+        moved = 5 * (n - 1) * s
+        cached = s > bench.SWEEP_LATENCY_MAX and n * s <= bench.LLC_BYTES
+        pts.append((s, moved, launches * alpha + moved / (2 * beta if cached else beta)))
+    a, b = bench.alpha_beta_fit(pts, launches, n)
+    assert a == pytest.approx(alpha) and b == pytest.approx(beta)
+    a1, b1 = bench.fit_line([p[1] for p in pts], [p[2] for p in pts])
+    assert abs(a1 / launches - alpha) > 0.1 * alpha or abs(1 / b1 - beta) > 0.1 * beta
