@@ -142,9 +142,11 @@ hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hi
 // Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
 // has checked that every rank pointer is 16-byte aligned, and for the
 // reduce-scatter layout also q % (16/elem) == 0); `nt` selects non-temporal
-// loads and stores (footprints beyond the last-level cache) over cached ones.
+// loads and stores (footprints beyond the last-level cache) over cached ones;
+// `rank_major` selects the rank-major all-reduce kernels (not the
+// reduce-scatter layout; needs vec, nt and 5..8 ranks).
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
-                               int grid_x, hipStream_t stream);
+                               bool rank_major, int grid_x, hipStream_t stream);
 
 // Fused all-gather: block p of send[p] (blk bytes) to recv[r] + p*blk for all r.
 hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream);

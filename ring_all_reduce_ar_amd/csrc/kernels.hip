@@ -8,13 +8,14 @@ using namespace detail;
 
 namespace {
 template <bool SC>
-hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, dim3 grid, hipStream_t s)
+hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, bool rank_major,
+                       dim3 grid, hipStream_t s)
 {
     switch (dtype) {
-    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, nt, grid, s);
-    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, nt, grid, s);
-    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, nt, grid, s);
-    case AR_INT32: return fused_op<I32, SC>(a, op, vec, nt, grid, s);
+    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, nt, rank_major, grid, s);
+    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, nt, rank_major, grid, s);
+    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, nt, rank_major, grid, s);
+    case AR_INT32: return fused_op<I32, SC>(a, op, vec, nt, rank_major, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -73,11 +74,12 @@ hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op,
 }
 
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
-                               int grid_x, hipStream_t stream)
+                               bool rank_major, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
-    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, grid, stream)
-                   : fused_dtype<false>(a, dtype, op, vec, nt, grid, stream);
+    if (scatter && rank_major) return hipErrorInvalidValue;
+    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, false, grid, stream)
+                   : fused_dtype<false>(a, dtype, op, vec, nt, rank_major, grid, stream);
 }
 
 hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream)

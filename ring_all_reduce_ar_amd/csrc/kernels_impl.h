@@ -384,7 +384,88 @@ __device__ __forceinline__ void fused_x2(const ReduceArgs& a, int c, uint64_t or
     }
 }
 
-template <class F, int OP, int NR, bool SCATTER, bool NT>
+// Tiles a rank-major thread folds together.
+constexpr int kRankMajorTiles = 4;
+
+// Rank-major body of the fused all-reduce (all-reduce layout, NR ranks known
+// at compile time): a thread takes M consecutive tiles per grid-stride step
+// and folds them one rank at a time in ring order, so each stage reads M
+// vectors from one rank buffer (a workgroup streams M * 4 KiB contiguous from
+// it), with the next rank's loads issued before the current rank's combine
+// (two stages in flight). Then all M results go to every rank. Each
+// element's fold is the ring order of the two-tile body. Between 128 MiB and
+// 4 GiB per rank at 5-8 ranks this measured 0-3.5 points above the two-tile
+// body on the same buffers (most at 256 MiB per rank), at 16 workgroups per
+// CU; at 14 GB per rank it measured -1.1 to +0.6, so it is not used there.
+template <class F, int OP, int NR, bool NT, int M>
+__device__ __forceinline__ void fused_rank_major(const ReduceArgs& a, int c, uint64_t org, uint64_t v0, uint64_t v1,
+                                                 uint64_t ntiles, uint64_t rot)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const uint64_t G = gridDim.x;
+    const uint64_t nsup = (ntiles + M - 1) / M;
+    const uint64_t srot = nsup ? (rot / M) % nsup : 0;
+    const void* sp[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) sp[k] = a.send[wrap_rank(c + k, NR)];
+    for (uint64_t st = blockIdx.x; st < nsup; st += G) {
+        const uint64_t sr = st + srot < nsup ? st + srot : st + srot - nsup;
+        uint64_t vv[M];
+        bool ok[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint64_t tile = sr * M + m;
+            vv[m] = org + tile * kBlock + threadIdx.x;
+            ok[m] = tile < ntiles && vv[m] >= v0 && vv[m] < v1;
+        }
+        Acc acc[M][E];
+        u32x4 xc[M], xn[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (ok[m]) xc[m] = ldv_at<NT>(sp[0], vv[m] * 16);
+#pragma unroll
+        for (int k = 1; k <= NR; ++k) {
+            // xc holds rank k-1 in fold order; load rank k before combining it
+            if (k < NR) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (ok[m]) xn[m] = ldv_at<NT>(sp[k], vv[m] * 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (ok[m]) {
+                    if (k == 1) {
+                        F::unpack(xc[m], acc[m]);
+                    } else {
+                        Acc t[E];
+                        F::unpack(xc[m], t);
+#pragma unroll
+                        for (int j = 0; j < E; ++j) acc[m][j] = combine<OP>(t[j], acc[m][j]);
+                    }
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            if (k < NR) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) xc[m] = xn[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            if (ok[m]) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], NR);
+                const u32x4 out = F::pack(acc[m]);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) stv<NT>(a.recv[r], vv[m], out);
+            }
+    }
+}
+
+// RM selects the rank-major body (its own kernel, so its registers do not
+// lower the occupancy of the two-tile one).
+template <class F, int OP, int NR, bool SCATTER, bool NT, bool RM = false>
 __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
 {
     using Acc = typename F::Acc;
@@ -414,7 +495,10 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     const uint64_t org = SCATTER ? v0 : v0 / kBlock * kBlock;
     const uint64_t ntiles = nv ? (v1 - 1 - org) / kBlock + 1 : 0;
     const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
-    if constexpr (NR > 0) {
+    if constexpr (RM) {
+        static_assert(NR > 0 && !SCATTER, "the rank-major body is for the all-reduce layout at fixed rank counts");
+        fused_rank_major<F, OP, NR, NT, kRankMajorTiles>(a, c, org, v0, v1, ntiles, rot);
+    } else if constexpr (NR > 0) {
         fused_x2<F, OP, NR, SCATTER, NT>(a, c, org, v0, v1, ntiles, rot);
     } else {
         // tiles t and t + G per iteration, as fused_x2 does
@@ -1105,9 +1189,31 @@ hipError_t fused_nr(const ReduceArgs& a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
-template <class F, int OP, bool SC>
-hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, dim3 grid, hipStream_t s)
+// The rank-major kernels: all-reduce layout, 16-byte vectors, non-temporal
+// access, 5..8 ranks (the host picks them only there).
+template <class F, int OP>
+hipError_t fused_nr_rank_major(const ReduceArgs& a, dim3 grid, hipStream_t s)
 {
+    const dim3 block(kBlock);
+    switch (a.n) {
+    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, false, true, true>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, false, true, true>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, false, true, true>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, false, true, true>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <class F, int OP, bool SC>
+hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, bool rank_major, dim3 grid, hipStream_t s)
+{
+    if constexpr (!SC) {
+        if (rank_major) {
+            if (!vec || !nt) return hipErrorInvalidValue;
+            return fused_nr_rank_major<F, OP>(a, grid, s);
+        }
+    }
     if (!vec) {
         hipLaunchKernelGGL((fused_reduce_scalar<F, OP, SC>), grid, dim3(kBlock), 0, s, a);
         return hipGetLastError();
@@ -1116,14 +1222,14 @@ hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, dim3 grid, hipStream_
 }
 
 template <class F, bool SC>
-hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, bool nt, dim3 grid, hipStream_t s)
+hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, bool nt, bool rank_major, dim3 grid, hipStream_t s)
 {
     switch (op) {
-    case AR_SUM: return fused_n<F, AR_SUM, SC>(a, vec, nt, grid, s);
-    case AR_AVG: return fused_n<F, AR_AVG, SC>(a, vec, nt, grid, s);
-    case AR_MAX: return fused_n<F, AR_MAX, SC>(a, vec, nt, grid, s);
-    case AR_MIN: return fused_n<F, AR_MIN, SC>(a, vec, nt, grid, s);
-    case AR_PROD: return fused_n<F, AR_PROD, SC>(a, vec, nt, grid, s);
+    case AR_SUM: return fused_n<F, AR_SUM, SC>(a, vec, nt, rank_major, grid, s);
+    case AR_AVG: return fused_n<F, AR_AVG, SC>(a, vec, nt, rank_major, grid, s);
+    case AR_MAX: return fused_n<F, AR_MAX, SC>(a, vec, nt, rank_major, grid, s);
+    case AR_MIN: return fused_n<F, AR_MIN, SC>(a, vec, nt, rank_major, grid, s);
+    case AR_PROD: return fused_n<F, AR_PROD, SC>(a, vec, nt, rank_major, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1234,8 +1340,8 @@ hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, int grid_x, hipStre
 // stepwise reduce-scatter, multi-tensor) in dtype_<name>.hip and the tree
 // kernels in tree_<name>.hip, so the build compiles them in parallel.
 #define AR_RING_INSTANTIATIONS(F, EXTERN)                                                                       \
-    EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t);      \
-    EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t);     \
+    EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, bool, dim3, hipStream_t); \
+    EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, bool, dim3, hipStream_t); \
     EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, dim3, hipStream_t);                       \
     EXTERN template hipError_t multi_op<F>(const MultiArgs&, ar_op_t, bool, int, hipStream_t);
 #define AR_TREE_INSTANTIATIONS(F, EXTERN)                                                           \

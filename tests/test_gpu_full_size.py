@@ -226,3 +226,37 @@ def test_generic_rank_counts_full_compare(n, dtype, op, extra):
             gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} rank {r}")
         del xs, exp, got, send, recv
     free()
+
+
+@pytest.mark.parametrize("n,dtype,op,count,inplace", [
+    (8, "f32", "sum", 35_000_003, False),
+    (5, "f16", "avg", 70_000_001, True),
+    (6, "bf16", "max", 67_108_869, True),  # 10 bytes above 128 MiB per rank
+    (7, "i32", "sum", 33_554_433, False),
+    (8, "f16", "prod", 67_108_880, True),
+])
+def test_rank_major_range_full_compare(n, dtype, op, count, inplace):
+    """Just above 128 MiB per rank at 5-8 ranks the all-reduce takes its
+    rank-major kernels (a thread folds four consecutive tiles one rank at a
+    time): every element of every rank against the oracle, with ragged chunks
+    and guard bands."""
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=count % 1000)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "fused", inplace=inplace)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} inplace={inplace} rank {r}")
+        del xs, exp, got, send, recv
+    free()
+
+
+@pytest.mark.parametrize("n,count,dtype", [(8, 1 << 30, "f32"), (8, (1 << 31) - 5, "f16"), (6, 999_999_997, "f32")])
+def test_rank_major_upper_sizes_sampled(n, count, dtype):
+    """At and below the rank-major kernels' 4 GiB-per-rank bound, in place as
+    the benchmark launches them: sampled elements (every chunk boundary
+    among them) against the oracle, all ranks identical."""
+    with ar.Comm(n, 0) as comm:
+        bufs = synthetic.rank_inputs("sweep", n, count, dtype, device="cuda", salt=7)
+        check_sampled(comm, bufs, dtype, "sum", "fused", seed=n)
+        del bufs
+    free()
