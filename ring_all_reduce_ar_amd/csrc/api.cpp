@@ -206,6 +206,8 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
 // non-temporal access) for more than 128 MiB and at most 4 GiB per rank, at
 // 16 workgroups per CU; measured against the two-tile kernels on the same
 // buffers: +2.4 to +3.5 points at 256 MiB per rank, about +0.5 at 1-4 GiB.
+// (The reduce-scatter takes them at every size beyond the cache; see
+// ar_reduce_scatter.)
 bool use_rank_major(size_t bytes_per_rank, int nranks, bool vec, bool nt)
 {
     return vec && nt && nranks >= 5 && nranks <= 8 && bytes_per_rank > (size_t(128) << 20) &&
@@ -696,15 +698,21 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
     if (!stepwise) {
         // 4 workgroups per CU at 1-2 ranks (2 ranks x 1 GiB: 76.4% against
         // 72.0% at 8), 8 above (best or within 1.5 points at 8 ranks)
-        const int gx_f = grid_for(comm, vec ? ceil_div(q, epv) : q, n, n <= 2 ? 4 : 8);
         ar::ReduceArgs a{};
         fill_ptrs(a, n, sendbufs, recvbufs);
         a.count = total;
         a.q = q;
         a.n = n;
         const bool nt = use_nt(footprint(n, sendbufs, recvbufs, sbytes, rbytes));
+        // Rank-major kernels at 5..8 ranks beyond the last-level cache: 16
+        // workgroups per CU up to 4 GiB of input per rank, 8 above (+9 points
+        // at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against the two-tile
+        // kernels on the same buffers).
+        const bool rank_major = vec && nt && n >= 5 && n <= 8;
+        const int per_cu = rank_major ? (sbytes <= (size_t(4) << 30) ? 16 : 8) : (n <= 2 ? 4 : 8);
+        const int gx_f = grid_for(comm, vec ? ceil_div(q, epv) : q, n, per_cu);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, false, gx_f, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, rank_major, gx_f, s);
             return err != hipSuccess ? err : tick(t);
         });
     }

@@ -143,8 +143,8 @@ hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hi
 // has checked that every rank pointer is 16-byte aligned, and for the
 // reduce-scatter layout also q % (16/elem) == 0); `nt` selects non-temporal
 // loads and stores (footprints beyond the last-level cache) over cached ones;
-// `rank_major` selects the rank-major all-reduce kernels (not the
-// reduce-scatter layout; needs vec, nt and 5..8 ranks).
+// `rank_major` selects the rank-major kernels (needs vec, nt and 5..8
+// ranks).
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
                                bool rank_major, int grid_x, hipStream_t stream);
 

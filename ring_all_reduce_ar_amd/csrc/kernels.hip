@@ -77,8 +77,7 @@ hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op
                                bool rank_major, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
-    if (scatter && rank_major) return hipErrorInvalidValue;
-    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, false, grid, stream)
+    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, rank_major, grid, stream)
                    : fused_dtype<false>(a, dtype, op, vec, nt, rank_major, grid, stream);
 }
 

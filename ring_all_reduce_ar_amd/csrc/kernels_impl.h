@@ -387,17 +387,19 @@ __device__ __forceinline__ void fused_x2(const ReduceArgs& a, int c, uint64_t or
 // Tiles a rank-major thread folds together.
 constexpr int kRankMajorTiles = 4;
 
-// Rank-major body of the fused all-reduce (all-reduce layout, NR ranks known
-// at compile time): a thread takes M consecutive tiles per grid-stride step
-// and folds them one rank at a time in ring order, so each stage reads M
-// vectors from one rank buffer (a workgroup streams M * 4 KiB contiguous from
-// it), with the next rank's loads issued before the current rank's combine
-// (two stages in flight). Then all M results go to every rank. Each
-// element's fold is the ring order of the two-tile body. Between 128 MiB and
-// 4 GiB per rank at 5-8 ranks this measured 0-3.5 points above the two-tile
-// body on the same buffers (most at 256 MiB per rank), at 16 workgroups per
-// CU; at 14 GB per rank it measured -1.1 to +0.6, so it is not used there.
-template <class F, int OP, int NR, bool NT, int M>
+// Rank-major body of the fused reduction (NR ranks known at compile time): a
+// thread takes M consecutive tiles per grid-stride step and folds them one
+// rank at a time in ring order, so each stage reads M vectors from one rank
+// buffer (a workgroup streams M * 4 KiB contiguous from it), with the next
+// rank's loads issued before the current rank's combine (two stages in
+// flight). Then the M results go to every rank (all-reduce) or to the
+// chunk's output block (SCATTER). Each element's fold is the ring order of
+// the two-tile body. Measured against the two-tile body on the same buffers
+// at 5-8 ranks: all-reduce +2.4 to +3.5 points at 256 MiB per rank, about
+// +0.5 at 1-4 GiB, -1.1 to +0.6 at 14 GB (so it stops at 4 GiB);
+// reduce-scatter +9 points at 256 MiB in per rank, +3.7 at 1 GiB, +1.5 at
+// 14 GB (at 8 workgroups per CU).
+template <class F, int OP, int NR, bool NT, int M, bool SCATTER = false>
 __device__ __forceinline__ void fused_rank_major(const ReduceArgs& a, int c, uint64_t org, uint64_t v0, uint64_t v1,
                                                  uint64_t ntiles, uint64_t rot)
 {
@@ -457,8 +459,12 @@ __device__ __forceinline__ void fused_rank_major(const ReduceArgs& a, int c, uin
 #pragma unroll
                 for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], NR);
                 const u32x4 out = F::pack(acc[m]);
+                if constexpr (SCATTER) {
+                    stv<NT>(a.recv[c], vv[m] - v0, out);
+                } else {
 #pragma unroll
-                for (int r = 0; r < NR; ++r) stv<NT>(a.recv[r], vv[m], out);
+                    for (int r = 0; r < NR; ++r) stv<NT>(a.recv[r], vv[m], out);
+                }
             }
     }
 }
@@ -496,8 +502,8 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     const uint64_t ntiles = nv ? (v1 - 1 - org) / kBlock + 1 : 0;
     const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
     if constexpr (RM) {
-        static_assert(NR > 0 && !SCATTER, "the rank-major body is for the all-reduce layout at fixed rank counts");
-        fused_rank_major<F, OP, NR, NT, kRankMajorTiles>(a, c, org, v0, v1, ntiles, rot);
+        static_assert(NR > 0, "the rank-major body is for fixed rank counts");
+        fused_rank_major<F, OP, NR, NT, kRankMajorTiles, SCATTER>(a, c, org, v0, v1, ntiles, rot);
     } else if constexpr (NR > 0) {
         fused_x2<F, OP, NR, SCATTER, NT>(a, c, org, v0, v1, ntiles, rot);
     } else {
@@ -1189,17 +1195,17 @@ hipError_t fused_nr(const ReduceArgs& a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
-// The rank-major kernels: all-reduce layout, 16-byte vectors, non-temporal
-// access, 5..8 ranks (the host picks them only there).
-template <class F, int OP>
+// The rank-major kernels: 16-byte vectors, non-temporal access, 5..8 ranks
+// (the host picks them only there), either layout.
+template <class F, int OP, bool SC>
 hipError_t fused_nr_rank_major(const ReduceArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 block(kBlock);
     switch (a.n) {
-    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, false, true, true>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, false, true, true>), grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, false, true, true>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, false, true, true>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, true>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, true>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, true>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, true>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1208,11 +1214,9 @@ hipError_t fused_nr_rank_major(const ReduceArgs& a, dim3 grid, hipStream_t s)
 template <class F, int OP, bool SC>
 hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, bool rank_major, dim3 grid, hipStream_t s)
 {
-    if constexpr (!SC) {
-        if (rank_major) {
-            if (!vec || !nt) return hipErrorInvalidValue;
-            return fused_nr_rank_major<F, OP>(a, grid, s);
-        }
+    if (rank_major) {
+        if (!vec || !nt) return hipErrorInvalidValue;
+        return fused_nr_rank_major<F, OP, SC>(a, grid, s);
     }
     if (!vec) {
         hipLaunchKernelGGL((fused_reduce_scalar<F, OP, SC>), grid, dim3(kBlock), 0, s, a);

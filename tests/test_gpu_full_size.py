@@ -260,3 +260,39 @@ def test_rank_major_upper_sizes_sampled(n, count, dtype):
         check_sampled(comm, bufs, dtype, "sum", "fused", seed=n)
         del bufs
     free()
+
+
+@pytest.mark.parametrize("n,dtype,op,rc,inplace", [
+    (8, "f32", "sum", 4_500_004, False),
+    (5, "f16", "avg", 14_000_008, True),
+    (7, "bf16", "max", 9_999_992, False),
+    (6, "i32", "sum", 6_000_004, True),
+])
+def test_reduce_scatter_rank_major_full_compare(n, dtype, op, rc, inplace):
+    """Reduce-scatter at 5-8 ranks beyond the last-level cache takes the
+    rank-major kernels (block lengths here are whole 16-byte vectors, as the
+    vector kernels need): every element of every rank's block against the
+    oracle's reduce-scatter, out of place or in place (recv[r] inside send[r]
+    at block r), with guard bands."""
+    xs = gu.make_inputs(n, n * rc, dtype, op, seed=rc % 1000)
+    exp = oracle.reduce_scatter([gu.host(x) for x in xs], dtype, op)
+    with ar.Comm(n, 0) as comm:
+        send = [gu.RankBuf(n * rc, dtype) for _ in range(n)]
+        for b, x in zip(send, xs):
+            b.view.copy_(x)
+        if inplace:
+            recv_ptrs = [send[r].sub_ptr(r * rc) for r in range(n)]
+            recv = []
+        else:
+            recv = [gu.RankBuf(rc, dtype) for _ in range(n)]
+            recv_ptrs = [b.ptr() for b in recv]
+        ar.ar_reduce_scatter(comm, [b.ptr() for b in send], recv_ptrs, rc, dtype, op, "fused")
+        torch.cuda.synchronize()
+        for b in send + recv:
+            assert b.guards_ok()
+        for r in range(n):
+            got = gu.host(send[r].view[r * rc:(r + 1) * rc]) if inplace else gu.host(recv[r].view)
+            gu.assert_same(got, exp[r], dtype, f"RS n={n} {dtype} {op} rc={rc} inplace={inplace} rank {r}")
+        del send, recv
+    del xs, exp
+    free()
