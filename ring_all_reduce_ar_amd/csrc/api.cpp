@@ -775,8 +775,13 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
         a.total = blk;
         a.n = n;
         const bool nt = use_nt(footprint(n, sendbufs, recvbufs, blk, rbytes));
+        // Rank-major copy at 5..8 ranks from 512 MiB of input per rank
+        // (measured against the copy above at 8 ranks: +7.4 points at
+        // 512 MiB, +1.0 at 1 GiB, +6.6 at 1.75 GB; 1-4 points slower at
+        // 64-256 MiB).
+        const bool rank_major = vec && nt && n >= 5 && n <= 8 && blk >= (size_t(512) << 20);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_gather(a, vec, nt, gx_f, s);
+            hipError_t err = ar::launch_fused_gather(a, vec, nt, rank_major, gx_f, s);
             return err != hipSuccess ? err : tick(t);
         });
     }

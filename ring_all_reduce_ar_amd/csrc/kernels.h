@@ -149,7 +149,8 @@ hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op
                                bool rank_major, int grid_x, hipStream_t stream);
 
 // Fused all-gather: block p of send[p] (blk bytes) to recv[r] + p*blk for all r.
-hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream);
+// `rank_major` selects the rank-major copy (needs vec and nt).
+hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, bool rank_major, int grid_x, hipStream_t stream);
 
 hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x, hipStream_t stream);
 

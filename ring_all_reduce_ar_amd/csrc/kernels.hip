@@ -81,9 +81,14 @@ hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op
                    : fused_dtype<false>(a, dtype, op, vec, nt, rank_major, grid, stream);
 }
 
-hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream)
+hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, bool rank_major, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
+    if (rank_major) {
+        if (!vec || !nt) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((fused_gather<true, true, true>), grid, dim3(kBlock), 0, stream, a);
+        return hipGetLastError();
+    }
     if (!vec) hipLaunchKernelGGL((fused_gather<false, true>), grid, dim3(kBlock), 0, stream, a);
     else if (nt) hipLaunchKernelGGL((fused_gather<true, true>), grid, dim3(kBlock), 0, stream, a);
     else hipLaunchKernelGGL((fused_gather<true, false>), grid, dim3(kBlock), 0, stream, a);

@@ -458,14 +458,18 @@ __device__ __forceinline__ void fused_rank_major(const ReduceArgs& a, int c, uin
             if (ok[m]) {
 #pragma unroll
                 for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], NR);
-                const u32x4 out = F::pack(acc[m]);
-                if constexpr (SCATTER) {
-                    stv<NT>(a.recv[c], vv[m] - v0, out);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) stv<NT>(a.recv[r], vv[m], out);
-                }
+                xc[m] = F::pack(acc[m]);
+                if constexpr (SCATTER) stv<NT>(a.recv[c], vv[m] - v0, xc[m]);
             }
+        if constexpr (!SCATTER) {
+            // rank by rank: the M results go to one buffer back to back
+            // (+0.6 to +1.3 points at 8 x 1 GiB against tile by tile)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (ok[m]) stv<NT>(a.recv[r], vv[m], xc[m]);
+        }
     }
 }
 
@@ -574,14 +578,38 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_scalar(const ReduceArgs a
 // ---------------------------------------------------------------------------
 // fused all-gather: block p of send[p] -> recv[r] + p*blk for every r
 // ---------------------------------------------------------------------------
-template <bool VEC, bool NT>
+// RM: each thread copies kRankMajorTiles consecutive 4 KiB tiles per
+// grid-stride step and stores them rank by rank, so a workgroup writes 16 KiB
+// back to back into one output buffer (measured +1 to +7.4 points at 512 MiB
+// to 1.75 GB of input per rank at 8 ranks, 1-4 points slower at 64-256 MiB).
+template <bool VEC, bool NT, bool RM = false>
 __global__ __launch_bounds__(kBlock) void fused_gather(const CopyArgs a)
 {
     const int p = blockIdx.y;
     const uint64_t blk = a.total;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if constexpr (VEC) {
+    if constexpr (RM) {
+        static_assert(VEC, "the rank-major copy takes 16-byte vectors");
+        constexpr int M = kRankMajorTiles;
+        const uint64_t nv = blk / 16, o = p * blk / 16;
+        const uint64_t nsup = (nv + M * kBlock - 1) / (M * kBlock);
+        for (uint64_t st = blockIdx.x; st < nsup; st += gridDim.x) {
+            u32x4 x[M];
+            uint64_t vv[M];
+            bool ok[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                vv[m] = (st * M + m) * kBlock + threadIdx.x;
+                ok[m] = vv[m] < nv;
+                if (ok[m]) x[m] = ldv<NT>(a.send[p], vv[m]);
+            }
+            for (int r = 0; r < a.n; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (ok[m]) stv<NT>(a.recv[r], o + vv[m], x[m]);
+        }
+    } else if constexpr (VEC) {
         const uint64_t nv = blk / 16, o = p * blk / 16;
         for (uint64_t v = t0; v < nv; v += stride) {
             const u32x4 x = ldv<NT>(a.send[p], v);

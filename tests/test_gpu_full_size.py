@@ -296,3 +296,36 @@ def test_reduce_scatter_rank_major_full_compare(n, dtype, op, rc, inplace):
         del send, recv
     del xs, exp
     free()
+
+
+@pytest.mark.parametrize("n,dtype,sc,inplace", [(5, "f32", 134_217_732, False), (8, "f16", 268_435_464, True)])
+def test_all_gather_rank_major_full_compare(n, dtype, sc, inplace):
+    """From 512 MiB of input per rank at 5-8 ranks the all-gather takes its
+    rank-major copy (four consecutive tiles per thread, stored rank by rank).
+    All-gather is concatenation in rank order (handbook "集合通信原语",
+    section 五个原语), so every output block of every rank is compared bit
+    for bit with its input block on the device; the tails are ragged and the
+    guard bands checked."""
+    xs = gu.make_inputs(n, sc, dtype, "sum", seed=n)
+    with ar.Comm(n, 0) as comm:
+        recv = [gu.RankBuf(n * sc, dtype) for _ in range(n)]
+        if inplace:
+            for r in range(n):
+                recv[r].view[r * sc:(r + 1) * sc].copy_(xs[r])
+            send_ptrs, send = [recv[r].sub_ptr(r * sc) for r in range(n)], []
+        else:
+            send = [gu.RankBuf(sc, dtype) for _ in range(n)]
+            for b, x in zip(send, xs):
+                b.view.copy_(x)
+            send_ptrs = [b.ptr() for b in send]
+        ar.ar_all_gather(comm, send_ptrs, [b.ptr() for b in recv], sc, dtype, "fused")
+        torch.cuda.synchronize()
+        for b in send + recv:
+            assert b.guards_ok()
+        iv = torch.int16 if gu.ESIZE[dtype] == 2 else torch.int32
+        for r in range(n):
+            for p in range(n):
+                assert torch.equal(recv[r].view[p * sc:(p + 1) * sc].view(iv), xs[p].view(iv)), (r, p)
+        del send, recv
+    del xs
+    free()
