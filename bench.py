@@ -31,7 +31,8 @@ Reported (one JSON line):
                saw per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
                plain copy's reading; one launch in fused mode, the sum of the
                2(N-1) launches in stepwise mode), from the committed profile
-               when it matches the current kernel source, else null
+               of that workload, mode and collective when it matches the
+               current kernel source, else null
   moved        stepwise and graph modes: the bytes the ring's steps move
                (5(N-1)*S for fp32/int32, (14N-18)*count with the fp32
                workspace of fp16/bf16) and their rate
@@ -146,10 +147,13 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, mode: str):
+def load_traffic(workload: str, mode: str, collective: str = "all_reduce"):
     """Per-launch HBM bytes from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.md")
+    on the current kernel source; else None. All-reduce summaries are
+    traffic_<workload>_<mode>.md, the other collectives'
+    traffic_<workload>_<mode>_<collective>.md."""
+    suffix = "" if collective == "all_reduce" else f"_{collective}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}{suffix}.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
@@ -474,7 +478,7 @@ def main():
     # move more and are reported against the same bytes, so modes compare.
     alg_bytes = (2 * n if coll in ("all_reduce", "all_to_all") else n + 1) * s_bytes
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, args.mode) if coll == "all_reduce" and not args.multi else None
+    traffic = None if args.multi else load_traffic(args.workload, args.mode, coll)
     result = {
         "metric": METRIC,
         "value": round(algbw, 3),
