@@ -57,3 +57,21 @@ def test_ring_moved_bytes_matches_the_step_walk():
     assert bench.ring_moved_bytes(8, 100, "f32") == 35 * 400
     assert bench.ring_moved_bytes(8, 100, "f16") == 94 * 100
     assert bench.ring_moved_bytes(1, 100, "f32") == 0
+
+
+def test_traffic_follows_collective_and_source_hash(monkeypatch, tmp_path):
+    """roofline.traffic comes from the counter summary of the same workload,
+    mode and collective, and only while the kernel sources still have the
+    hash recorded in it."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic_w_fused.md").write_text("kernel_sha: abc123\ntraffic_bytes_per_launch: 2.5e+10\n")
+    (prof / "traffic_w_fused_all_gather.md").write_text("kernel_sha: abc123\ntraffic_bytes_per_launch: 1.5e+10\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_sha", lambda: "abc123")
+    assert bench.load_traffic("w", "fused") == 2.5e10
+    assert bench.load_traffic("w", "fused", "all_gather") == 1.5e10
+    assert bench.load_traffic("w", "fused", "reduce_scatter") is None
+    assert bench.load_traffic("w", "stepwise") is None
+    monkeypatch.setattr(bench, "kernel_sha", lambda: "def456")
+    assert bench.load_traffic("w", "fused") is None
