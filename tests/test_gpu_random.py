@@ -97,3 +97,27 @@ def test_random_all_gather_and_all_to_all(case):
         for r in range(n):
             assert a_out[r].guards_ok()
             gu.assert_same(gu.host(a_out[r].view), a_exp[r], dtype, f"all-to-all case {case} rank {r}")
+
+
+def _large_cases(seed, k):
+    rng = np.random.default_rng(seed)
+    for i in range(k):
+        n = int(rng.integers(5, 9))
+        dtype = DTYPES[int(rng.integers(4))]
+        nbytes = int(rng.integers(130 << 20, 600 << 20))
+        count = nbytes // gu.ESIZE[dtype] - int(rng.integers(0, 9))
+        yield (i, n, count, dtype, OPS[int(rng.integers(5))])
+
+
+@pytest.mark.parametrize("case", list(_large_cases(31, 10)), ids=lambda c: f"big{c[0]}-n{c[1]}-{c[3]}-{c[4]}")
+def test_random_large_all_reduce_sampled(case):
+    """130-600 MB per rank at 5-8 ranks (the rank-major, non-temporal kernels),
+    in place: sampled elements (every chunk boundary among them) against the
+    oracle, all ranks identical."""
+    import test_gpu_full_size as fs
+    i, n, count, dtype, op = case
+    with ar.Comm(n, 0) as comm:
+        bufs = gu.make_inputs(n, count, dtype, op, seed=4000 + i)
+        fs.check_sampled(comm, bufs, dtype, op, "fused", seed=i)
+        del bufs
+    fs.free()
