@@ -112,6 +112,66 @@ def test_multi_generic_rank_count_both_tile_halves(n):
             check(comm, sizes, dtype, op, seed=n + 1, inplace=True)
 
 
+@pytest.mark.parametrize("n", [8, 17, 64])
+def test_multi_views_of_flat_buckets(n):
+    """In-place tensors that are views into one flat buffer per rank, at the
+    same offsets on every rank (the DDP layout), share one block of base
+    pointers in the kernel arguments. Mixed sizes listed out of memory order,
+    a base shifted off 16-byte alignment, and one tensor in its own
+    allocation in the same call: against the oracle's fold over the bucket
+    in the listed order, with guard bands."""
+    for dtype, op, shift in (("f32", "sum", 0), ("bf16", "avg", 2), ("f16", "max", 6), ("i32", "prod", 4)):
+        e = gu.ESIZE[dtype]
+        sizes = [3, 40_000, 1, 123_457, 7, 65_536, n * 513]
+        gap = 3  # elements between neighbouring views
+        order = [4, 0, 6, 2, 5, 1, 3]  # memory order of the listed tensors
+        starts = {}
+        pos = 0
+        for t in order:
+            starts[t] = pos
+            pos += sizes[t] + gap
+        extra = 10_001  # this tensor gets its own allocation per rank
+        total = sum(sizes) + extra
+        flat_in = gu.make_inputs(n, total, dtype, op, seed=n + 5)
+        bufs = [gu.RankBuf(pos + 8, dtype, offset=shift) for _ in range(n)]
+        own = [gu.RankBuf(extra, dtype) for _ in range(n)]
+        rows, off = [], 0
+        listed = sizes[:3] + [extra] + sizes[3:]
+        for t, c in enumerate(listed):
+            if t == 3:
+                for r in range(n):
+                    own[r].view.copy_(flat_in[r][off:off + c])
+                rows.append([own[r].ptr() for r in range(n)])
+            else:
+                k = t if t < 3 else t - 1
+                for r in range(n):
+                    bufs[r].view[starts[k]:starts[k] + c].copy_(flat_in[r][off:off + c])
+                rows.append([bufs[r].sub_ptr(starts[k]) for r in range(n)])
+            off += c
+        with ar.Comm(n, 0) as comm:
+            ar.ar_all_reduce_multi(comm, rows, rows, listed, dtype, op)
+            torch.cuda.synchronize()
+        for b in bufs + own:
+            assert b.guards_ok()
+        exp = oracle.fold_all_reduce([gu.host(x) for x in flat_in], dtype, op)
+        for r in range(n):
+            parts, off = [], 0
+            for t, c in enumerate(listed):
+                if t == 3:
+                    parts.append(gu.host(own[r].view))
+                else:
+                    k = t if t < 3 else t - 1
+                    parts.append(gu.host(bufs[r].view[starts[k]:starts[k] + c]))
+                off += c
+            gu.assert_same(np.concatenate(parts), exp[r], dtype, f"views n={n} {dtype} {op} rank {r}")
+            # the gaps between views (filled with 0xFF bytes, never part of a
+            # tensor) are untouched
+            host = np.ascontiguousarray(gu.host(bufs[r].view))
+            for k in order:
+                g0 = starts[k] + sizes[k]
+                assert np.all(host[g0:g0 + gap].view(np.uint8) == 0xFF), (n, dtype, r, k)
+
+
 def test_multi_single_tensor_spanning_all_chunks():
     with ar.Comm(8, 0) as comm:
         check(comm, [8 * 50000 + 7], "f16", "sum", seed=4)
