@@ -950,15 +950,20 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
         TensorPlan tp;
         // 16-byte vectors need every rank's send and recv pointer at the same
         // offset from a 16-byte boundary; a0 elements precede the first one.
-        const uintptr_t mis = reinterpret_cast<uintptr_t>(sendbufs[static_cast<size_t>(t) * n]) % 16;
-        bool vec = true, inplace = true;
+        // When the pointers also share their offset from a 128-byte line
+        // (views at one offset into line-aligned per-rank buckets), the
+        // vectors start on the first whole line instead, so that a wave's
+        // 1 KiB access covers eight lines, not nine.
+        const uintptr_t mis = reinterpret_cast<uintptr_t>(sendbufs[static_cast<size_t>(t) * n]) % 128;
+        bool vec = true, line = true, inplace = true;
         for (int r = 0; r < n; ++r) {
-            const void* sp = sendbufs[static_cast<size_t>(t) * n + r];
-            const void* dp = recvbufs[static_cast<size_t>(t) * n + r];
-            vec = vec && reinterpret_cast<uintptr_t>(sp) % 16 == mis && reinterpret_cast<uintptr_t>(dp) % 16 == mis;
+            const uintptr_t sp = reinterpret_cast<uintptr_t>(sendbufs[static_cast<size_t>(t) * n + r]);
+            const uintptr_t dp = reinterpret_cast<uintptr_t>(recvbufs[static_cast<size_t>(t) * n + r]);
+            vec = vec && sp % 16 == mis % 16 && dp % 16 == mis % 16;
+            line = line && sp % 128 == mis && dp % 128 == mis;
             inplace = inplace && sp == dp;
         }
-        const uint64_t a0 = (16 - mis) % 16 / e;
+        const uint64_t a0 = (line ? (128 - mis) % 128 : (16 - mis % 16) % 16) / e;
         for (int r = 0; r < n; ++r) tp.ptrs.push_back(sendbufs[static_cast<size_t>(t) * n + r]);
         if (!inplace)
             for (int r = 0; r < n; ++r) tp.ptrs.push_back(recvbufs[static_cast<size_t>(t) * n + r]);
@@ -994,7 +999,8 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
                 uint64_t nt;
                 if (pc.flags & ar::kPieceVec) {
                     uint64_t vb, ve;
-                    ar::piece_vectors(pc.j0, pc.j0 + pc.len, (pc.flags >> ar::kPieceShiftBit) & 7u, E, &vb, &ve);
+                    ar::piece_vectors(pc.j0, pc.j0 + pc.len, (pc.flags >> ar::kPieceShiftBit) & ar::kPieceShiftMask, E,
+                                      &vb, &ve);
                     nt = std::max<uint64_t>(1, ceil_div(ve - vb, ar::kMultiVecTile));
                 } else {
                     nt = ceil_div(pc.len, ar::kBlock);

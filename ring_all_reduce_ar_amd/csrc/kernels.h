@@ -83,17 +83,23 @@ hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int
 // are numbered across pieces.
 constexpr uint8_t kPieceVec = 1;      // 16-byte vectors in the body, elements at the ends
 constexpr uint8_t kPieceInPlace = 2;  // recv pointers are the send pointers
-constexpr int kPieceShiftBit = 2;     // bits 2..4: a0, the tensor's first 16-byte aligned element
+constexpr int kPieceShiftBit = 2;     // bits 2..7: a0, the tensor's first element of its aligned run
+constexpr unsigned kPieceShiftMask = 63;
+// 16-byte vectors per 128-byte cache line.
+constexpr uint64_t kLineVectors = 8;
 
 // The 16-byte vectors of a piece [j0, j_end) of a tensor whose element a0 is
-// the first one on a 16-byte boundary (the same a0 for every rank's
-// pointers): vector k holds elements [a0 + kE, a0 + (k+1)E), and the piece's
-// whole vectors are [vb, ve). Shared by the planner and the kernel, which
-// must agree on the tile count.
+// the first one on a 128-byte line when every rank's pointers share one
+// offset from a line, else the first one on a 16-byte boundary (the same a0
+// for every rank's pointers): vector k holds elements [a0 + kE, a0 + (k+1)E),
+// and the piece's whole vectors are [vb, ve), vb a multiple of a line's
+// vectors so that the piece's tiles start on a line when a0 does. Shared by
+// the planner and the kernel, which must agree on the tile count.
 __host__ __device__ inline void piece_vectors(uint64_t j0, uint64_t j_end, uint64_t a0, uint64_t E, uint64_t* vb,
                                               uint64_t* ve)
 {
-    *vb = j0 <= a0 ? 0 : (j0 - a0 + E - 1) / E;
+    const uint64_t L = kLineVectors * E;
+    *vb = j0 <= a0 ? 0 : (j0 - a0 + L - 1) / L * kLineVectors;
     *ve = j_end <= a0 ? 0 : (j_end - a0) / E;
     if (*ve < *vb) *ve = *vb;
 }

@@ -1107,7 +1107,7 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
         if (pc.flags & kPieceVec) {
             // vector k holds elements [a0 + kE, a0 + (k+1)E): its address is
             // base + a0 * sizeof(element) + 16k, aligned on every rank
-            const uint64_t a0 = (pc.flags >> kPieceShiftBit) & 7u;
+            const uint64_t a0 = (pc.flags >> kPieceShiftBit) & kPieceShiftMask;
             const uint64_t boff = a0 * (16 / E);
             uint64_t vb, ve;
             piece_vectors(pc.j0, j_end, a0, E, &vb, &ve);
@@ -1143,7 +1143,8 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
                         for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], off[u], out[u]);
             }
             if (ti == 0) {
-                // elements before the first whole vector and after the last
+                // elements before the first whole vector (fewer than a line's)
+                // and after the last (fewer than a vector's)
                 const uint64_t vstart = a0 + vb * E, vend = a0 + ve * E;
                 const uint64_t head_end = vstart < j_end ? (vstart > pc.j0 ? vstart : pc.j0) : j_end;
                 const uint64_t nhead = head_end - pc.j0;
