@@ -88,6 +88,37 @@ def test_multi_shifted_and_mixed_alignment(dtype):
             check(comm, sizes, dtype, "prod", seed=301, offset=lambda t, r, side: side * e)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "i32"])
+def test_multi_line_and_16_byte_vector_starts(dtype):
+    """Rank pointers at one offset from a 128-byte line: vectors start on the
+    first whole line, up to 128/e - 1 elements in (offsets chosen so that the
+    first vector is 0, 1, 2, ... and 128/e - 1 elements in). Pointers that
+    share their 16-byte offset but sit at different offsets from a line on
+    different ranks or sides: vectors start on the first 16-byte boundary.
+    Pieces of every length around a line, across chunk boundaries and over
+    several tiles."""
+    e = gu.ESIZE[dtype]
+    epv = gu.EPV[dtype]
+    line = 128 // e
+    sizes = [1, line - 1, line + 1, 3 * epv + 2, 2 * 256 * epv + 5, 0, 7, 4 * 256 * epv + epv - 1, 2,
+             1000 * epv + 3, 2 * line + 1]
+    # a buffer's address is a 512-byte aligned allocation plus the 64-byte
+    # guard plus its offset: these offsets put its first whole line 0, e, 2e,
+    # ..., 128 - e bytes away
+    lead = sorted({0, e, 2 * e, 16 - e, 16, 64 - e, 64, 64 + e, 112, 128 - e})
+    for n in (3, 8):
+        with ar.Comm(n, 0) as comm:
+            for i, b in enumerate(lead):
+                o = (64 - b) % 128
+                check(comm, sizes, dtype, "sum", seed=400 + i, offset=o, inplace=i % 2 == 1)
+            for k in (0, 1, epv - 1):
+                at = (lambda k: lambda t, r, side: 16 * ((t + r + 3 * side) % 8) + k * e)(k)
+                check(comm, sizes, dtype, "max", seed=500 + k, offset=at)
+                at_in = (lambda k: lambda t, r, side: 16 * ((t + r) % 8) + k * e)(k)
+                check(comm, sizes, dtype, "avg" if dtype != "i32" else "min", seed=600 + k, offset=at_in,
+                      inplace=True)
+
+
 def test_multi_many_tensors_many_launches():
     """300 tensors at 8 ranks and 40 tensors at 64 ranks take several
     kernel-argument batches each."""
@@ -115,11 +146,12 @@ def test_multi_generic_rank_count_both_tile_halves(n):
 @pytest.mark.parametrize("n", [8, 17, 64])
 def test_multi_views_of_flat_buckets(n):
     """In-place tensors that are views into one flat buffer per rank, at the
-    same offsets on every rank (the DDP layout), share one block of base
-    pointers in the kernel arguments. Mixed sizes listed out of memory order,
-    a base shifted off 16-byte alignment, and one tensor in its own
-    allocation in the same call: against the oracle's fold over the bucket
-    in the listed order, with guard bands."""
+    same offsets on every rank (the DDP layout): every view shares its offset
+    from a 128-byte line across ranks, so its vectors start on a line. Mixed
+    sizes listed out of memory order, a base shifted off 16-byte alignment,
+    and one tensor in its own allocation in the same call: against the
+    oracle's fold over the bucket in the listed order, with guard bands and
+    untouched gaps."""
     for dtype, op, shift in (("f32", "sum", 0), ("bf16", "avg", 2), ("f16", "max", 6), ("i32", "prod", 4)):
         e = gu.ESIZE[dtype]
         sizes = [3, 40_000, 1, 123_457, 7, 65_536, n * 513]
