@@ -981,6 +981,15 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
         off += cnt;
     }
 
+    uint64_t touched = 0;
+    for (const Interval& x : iv) touched += x.hi - x.lo;
+    const bool nt = use_nt(touched);
+    // The rank-major kernel at 8 ranks, on the flat call's size rule (the
+    // bucket's bytes per rank); its vector tiles are four kBlock-vector
+    // quarters wide.
+    const bool rank_major = n == 8 && use_rank_major(total * e, n, true, nt);
+    const uint64_t tile_vecs = rank_major ? ar::kMultiRankMajorTile : ar::kMultiVecTile;
+
     // Lays out tensors [t0, t1) of the plan as one table (pointer blocks,
     // then pieces with their first tiles) and returns its header.
     auto layout = [&](size_t t0, size_t t1, unsigned char* out, ar::MultiHeader* h) -> bool {
@@ -996,16 +1005,16 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
             for (ar::MultiPiece pc : plan[t].pieces) {
                 pc.tile0 = static_cast<uint32_t>(tiles);
                 pc.ptrs = static_cast<uint16_t>(p0);
-                uint64_t nt;
+                uint64_t piece_tiles;
                 if (pc.flags & ar::kPieceVec) {
                     uint64_t vb, ve;
                     ar::piece_vectors(pc.j0, pc.j0 + pc.len, (pc.flags >> ar::kPieceShiftBit) & ar::kPieceShiftMask, E,
                                       &vb, &ve);
-                    nt = std::max<uint64_t>(1, ceil_div(ve - vb, ar::kMultiVecTile));
+                    piece_tiles = std::max<uint64_t>(1, ceil_div(ve - vb, tile_vecs));
                 } else {
-                    nt = ceil_div(pc.len, ar::kBlock);
+                    piece_tiles = ceil_div(pc.len, ar::kBlock);
                 }
-                tiles += nt;
+                tiles += piece_tiles;
                 std::memcpy(out + h->pieces_offset + static_cast<size_t>(np) * sizeof(pc), &pc, sizeof(pc));
                 ++np;
             }
@@ -1022,9 +1031,6 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
         return bytes;
     };
 
-    uint64_t touched = 0;
-    for (const Interval& x : iv) touched += x.hi - x.lo;
-    const bool nt = use_nt(touched);
     // 16 workgroups per CU: the 29-tensor 256 MiB bucket ran at 7.09 ms at 64
     // ranks (flat: 7.05) against 7.51 at 8 per CU, and 0.913 against 0.929 ms
     // at 8 ranks.
@@ -1046,12 +1052,13 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
         t0 = t1;
     }
     if (comm->debug)
-        std::fprintf(stderr, "[allreduce] all_reduce_multi n=%d tensors=%zu dtype=%s op=%d batches=%zu\n",
-                     n, plan.size(), dtype_name(dtype), static_cast<int>(op), batches.size());
+        std::fprintf(stderr, "[allreduce] all_reduce_multi n=%d tensors=%zu dtype=%s op=%d batches=%zu rank_major=%d\n",
+                     n, plan.size(), dtype_name(dtype), static_cast<int>(op), batches.size(), rank_major ? 1 : 0);
     return run_eager(comm, stream, static_cast<int>(batches.size()), [&](hipStream_t s, StepTimer* t) {
         for (const auto& a : batches) {
             hipError_t e2 =
-                ar::launch_multi_reduce(a, dtype, op, nt, static_cast<int>(std::min<uint64_t>(a.h.ntiles, cap)), s);
+                ar::launch_multi_reduce(a, dtype, op, nt, rank_major,
+                                        static_cast<int>(std::min<uint64_t>(a.h.ntiles, cap)), s);
             if (e2 == hipSuccess) e2 = tick(t);
             if (e2 != hipSuccess) return e2;
         }

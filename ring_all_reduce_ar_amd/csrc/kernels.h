@@ -114,8 +114,10 @@ struct MultiPiece {
 static_assert(sizeof(MultiPiece) == 24, "MultiPiece layout");
 constexpr int kMultiBlobBytes = 3840;
 // Vector pieces are cut into tiles of two kBlock-vector halves (a thread
-// takes one vector in each); element pieces into tiles of kBlock elements.
+// takes one vector in each), or of four for the rank-major kernel; element
+// pieces into tiles of kBlock elements.
 constexpr int kMultiVecTile = 2 * kBlock;
+constexpr int kMultiRankMajorTile = 4 * kBlock;
 struct MultiHeader {
     int n;
     int npieces;
@@ -129,7 +131,9 @@ struct MultiArgs {
     alignas(16) unsigned char blob[kMultiBlobBytes];
 };
 
-hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, int grid_x,
+// `rank_major` selects the rank-major kernel (needs nt and 8 ranks; the
+// table's vector tiles are then kMultiRankMajorTile vectors wide).
+hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, bool rank_major, int grid_x,
                                hipStream_t stream);
 
 // All-to-all block copies: row y copies block p of send[r] to block r of

@@ -61,14 +61,14 @@ hipError_t launch_tree_bcast_level(const TreeArgs& a, size_t elem, bool vec, int
 
 
 
-hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, int grid_x,
+hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, bool rank_major, int grid_x,
                                hipStream_t stream)
 {
     switch (dtype) {
-    case AR_FLOAT32: return multi_op<F32>(a, op, nt, grid_x, stream);
-    case AR_FLOAT16: return multi_op<F16>(a, op, nt, grid_x, stream);
-    case AR_BFLOAT16: return multi_op<BF16>(a, op, nt, grid_x, stream);
-    case AR_INT32: return multi_op<I32>(a, op, nt, grid_x, stream);
+    case AR_FLOAT32: return multi_op<F32>(a, op, nt, rank_major, grid_x, stream);
+    case AR_FLOAT16: return multi_op<F16>(a, op, nt, rank_major, grid_x, stream);
+    case AR_BFLOAT16: return multi_op<BF16>(a, op, nt, rank_major, grid_x, stream);
+    case AR_INT32: return multi_op<I32>(a, op, nt, rank_major, grid_x, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -1062,7 +1062,9 @@ __device__ __forceinline__ int multi_find_piece(cpiece* pieces, int npieces, uin
 // tensor (pointers) are uniform across the workgroup. A workgroup's tiles
 // only increase, so after a binary search for its first tile it finds the
 // next piece by scanning forward. NR > 0 fixes the rank count at compile time.
-template <class F, int OP, int NR, bool NT>
+// RM (with NR > 0) selects the rank-major vector tile: four kBlock-vector
+// quarters per tile, folded one rank at a time as in the flat rank-major body.
+template <class F, int OP, int NR, bool NT, bool RM = false>
 __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned char* table)
 {
     using Acc = typename F::Acc;
@@ -1111,36 +1113,97 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
             const uint64_t boff = a0 * (16 / E);
             uint64_t vb, ve;
             piece_vectors(pc.j0, j_end, a0, E, &vb, &ve);
-            // the tile's two halves: vectors v and v + kBlock of this thread
-            const uint64_t v = vb + static_cast<uint64_t>(ti) * kMultiVecTile + threadIdx.x;
-            const bool ok[2] = {v < ve, v + kBlock < ve};
-            if constexpr (NR > 0) {
-                // all 2*NR loads in flight before either fold
+            if constexpr (RM && NR > 0) {
+                // the tile's four quarters: vectors v + m * kBlock of this
+                // thread; each stage loads them from one rank, the next
+                // rank's loads issued before the current rank's combine
+                constexpr int M = kMultiRankMajorTile / kBlock;
+                const uint64_t v = vb + static_cast<uint64_t>(ti) * kMultiRankMajorTile + threadIdx.x;
                 const void* sp[NR];
 #pragma unroll
                 for (int k = 0; k < NR; ++k) sp[k] = send[wrap_rank(c + k, NR)];
-                u32x4 x[2][NR];
+                uint64_t off[M];
+                bool ok[M];
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    if (ok[u]) {
+                for (int m = 0; m < M; ++m) {
+                    off[m] = (v + m * kBlock) * 16 + boff;
+                    ok[m] = v + m * kBlock < ve;
+                }
+                Acc acc[M][E];
+                u32x4 xc[M], xn[M];
 #pragma unroll
-                        for (int k = 0; k < NR; ++k) x[u][k] = ldv_at<NT>(sp[k], (v + u * kBlock) * 16 + boff);
+                for (int m = 0; m < M; ++m)
+                    if (ok[m]) xc[m] = ldv_at<NT>(sp[0], off[m]);
+#pragma unroll
+                for (int k = 1; k <= NR; ++k) {
+                    if (k < NR) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+                            if (ok[m]) xn[m] = ldv_at<NT>(sp[k], off[m]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        if (ok[m]) {
+                            if (k == 1) {
+                                F::unpack(xc[m], acc[m]);
+                            } else {
+                                Acc t[E];
+                                F::unpack(xc[m], t);
+#pragma unroll
+                                for (int j = 0; j < E; ++j) acc[m][j] = combine<OP>(t[j], acc[m][j]);
+                            }
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (k < NR) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m) xc[m] = xn[m];
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (ok[m]) {
+#pragma unroll
+                        for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], NR);
+                        xc[m] = F::pack(acc[m]);
                     }
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    if (ok[u]) {
-                        const u32x4 out = fold_loaded<F, OP, NR>(x[u]);
+                for (int r = 0; r < NR; ++r)
 #pragma unroll
-                        for (int r = 0; r < NR; ++r) stv_at<NT>(recv[r], (v + u * kBlock) * 16 + boff, out);
-                    }
+                    for (int m = 0; m < M; ++m)
+                        if (ok[m]) stv_at<NT>(recv[r], off[m], xc[m]);
             } else {
-                const uint64_t off[2] = {v * 16 + boff, (v + kBlock) * 16 + boff};
-                u32x4 out[2];
-                fold_pair_any<F, OP, NT>(send, c, n, off, ok, out);
+                // the tile's two halves: vectors v and v + kBlock of this thread
+                const uint64_t v = vb + static_cast<uint64_t>(ti) * kMultiVecTile + threadIdx.x;
+                const bool ok[2] = {v < ve, v + kBlock < ve};
+                if constexpr (NR > 0) {
+                    // all 2*NR loads in flight before either fold
+                    const void* sp[NR];
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    if (ok[u])
-                        for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], off[u], out[u]);
+                    for (int k = 0; k < NR; ++k) sp[k] = send[wrap_rank(c + k, NR)];
+                    u32x4 x[2][NR];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        if (ok[u]) {
+#pragma unroll
+                            for (int k = 0; k < NR; ++k) x[u][k] = ldv_at<NT>(sp[k], (v + u * kBlock) * 16 + boff);
+                        }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        if (ok[u]) {
+                            const u32x4 out = fold_loaded<F, OP, NR>(x[u]);
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) stv_at<NT>(recv[r], (v + u * kBlock) * 16 + boff, out);
+                        }
+                } else {
+                    const uint64_t off[2] = {v * 16 + boff, (v + kBlock) * 16 + boff};
+                    u32x4 out[2];
+                    fold_pair_any<F, OP, NT>(send, c, n, off, ok, out);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        if (ok[u])
+                            for (int r = 0; r < n; ++r) stv_at<NT>(recv[r], off[u], out[u]);
+                }
             }
             if (ti == 0) {
                 // elements before the first whole vector (fewer than a line's)
@@ -1169,10 +1232,10 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
     }
 }
 
-template <class F, int OP, int NR, bool NT>
+template <class F, int OP, int NR, bool NT, bool RM = false>
 __global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
 {
-    multi_body<F, OP, NR, NT>(a.h, a.blob);
+    multi_body<F, OP, NR, NT, RM>(a.h, a.blob);
 }
 
 // ---------------------------------------------------------------------------
@@ -1342,31 +1405,38 @@ hipError_t tree_level_op(const TreeArgs& a, ar_op_t op, bool vec, dim3 grid, hip
 }
 
 template <class F, int OP, bool NT>
-hipError_t multi_nr(const MultiArgs& a, int grid_x, hipStream_t s)
+hipError_t multi_nr(const MultiArgs& a, bool rank_major, int grid_x, hipStream_t s)
 {
     const dim3 grid(grid_x), block(kBlock);
-    if (a.h.n == 8) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT>), grid, block, 0, s, a);
+    if (rank_major) {
+        // the rank-major kernel exists for 8 ranks with non-temporal access
+        if (!NT || a.h.n != 8) return hipErrorInvalidValue;
+        if constexpr (NT) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT, true>), grid, block, 0, s, a);
+    } else if (a.h.n == 8) {
+        hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
 template <class F, bool NT>
-hipError_t multi_nt(const MultiArgs& a, ar_op_t op, int grid_x, hipStream_t s)
+hipError_t multi_nt(const MultiArgs& a, ar_op_t op, bool rank_major, int grid_x, hipStream_t s)
 {
     switch (op) {
-    case AR_SUM: return multi_nr<F, AR_SUM, NT>(a, grid_x, s);
-    case AR_AVG: return multi_nr<F, AR_AVG, NT>(a, grid_x, s);
-    case AR_MAX: return multi_nr<F, AR_MAX, NT>(a, grid_x, s);
-    case AR_MIN: return multi_nr<F, AR_MIN, NT>(a, grid_x, s);
-    case AR_PROD: return multi_nr<F, AR_PROD, NT>(a, grid_x, s);
+    case AR_SUM: return multi_nr<F, AR_SUM, NT>(a, rank_major, grid_x, s);
+    case AR_AVG: return multi_nr<F, AR_AVG, NT>(a, rank_major, grid_x, s);
+    case AR_MAX: return multi_nr<F, AR_MAX, NT>(a, rank_major, grid_x, s);
+    case AR_MIN: return multi_nr<F, AR_MIN, NT>(a, rank_major, grid_x, s);
+    case AR_PROD: return multi_nr<F, AR_PROD, NT>(a, rank_major, grid_x, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <class F>
-hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, int grid_x, hipStream_t s)
+hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, bool rank_major, int grid_x, hipStream_t s)
 {
-    return nt ? multi_nt<F, true>(a, op, grid_x, s) : multi_nt<F, false>(a, op, grid_x, s);
+    return nt ? multi_nt<F, true>(a, op, rank_major, grid_x, s) : multi_nt<F, false>(a, op, rank_major, grid_x, s);
 }
 
 // Per-dtype entry points, each instantiated once: the ring kernels (fused,
@@ -1376,7 +1446,7 @@ hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, int grid_x, hipStre
     EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, bool, dim3, hipStream_t); \
     EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, bool, dim3, hipStream_t); \
     EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, dim3, hipStream_t);                       \
-    EXTERN template hipError_t multi_op<F>(const MultiArgs&, ar_op_t, bool, int, hipStream_t);
+    EXTERN template hipError_t multi_op<F>(const MultiArgs&, ar_op_t, bool, bool, int, hipStream_t);
 #define AR_TREE_INSTANTIATIONS(F, EXTERN)                                                           \
     EXTERN template hipError_t tree_op<F>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t); \
     EXTERN template hipError_t tree_level_op<F>(const TreeArgs&, ar_op_t, bool, dim3, hipStream_t);

@@ -253,6 +253,61 @@ def test_bucket64_mixed_tensors_full_size(op):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,op,shift", [("f32", "sum", 3), ("bf16", "avg", 0), ("f32", "max", 1),
+                                            ("i32", "sum", 2)])
+def test_bucket8_rank_major_multi_full_compare(dtype, op, shift):
+    """8 ranks with more than 128 MiB of bucket per rank take the rank-major
+    multi-tensor kernel (four-quarter tiles). Views of log-uniform sizes into
+    one allocation per rank, its base shifted `shift` elements off a line:
+    every element against the oracle's fold over the flat bucket, and bit for
+    bit against the flat call."""
+    n = 8
+    e = gu.ESIZE[dtype]
+    count = (160 << 20) // e + 12_345
+    sizes = synthetic.bucket_sizes(count, e, 4096, 64 << 20, seed=9)
+    assert sum(sizes) == count
+    flat_in = gu.make_inputs(n, count, dtype, op, seed=77)
+    bufs = [gu.RankBuf(count, dtype, offset=shift * e) for _ in range(n)]
+    for r in range(n):
+        bufs[r].view.copy_(flat_in[r])
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    rows = [[bufs[r].sub_ptr(int(o)) for r in range(n)] for o in offs]
+    flat = [x.clone() for x in flat_in]
+    with ar.Comm(n, 0) as comm:
+        ar.ar_all_reduce_multi(comm, rows, rows, sizes, dtype, op)
+        fp = [b.data_ptr() for b in flat]
+        ar.ar_all_reduce(comm, fp, fp, count, dtype, op, "fused")
+        torch.cuda.synchronize()
+    exp = oracle.fold_all_reduce([gu.host(x) for x in flat_in], dtype, op)
+    for r in range(n):
+        assert bufs[r].guards_ok(), f"rank {r} guard"
+        got = gu.host(bufs[r].view)
+        gu.assert_same(got, exp[r], dtype, f"rank-major multi {dtype} {op} rank {r} vs oracle")
+        gu.assert_same(got, gu.host(flat[r]), dtype, f"rank-major multi {dtype} {op} rank {r} vs flat")
+    print(f"{len(sizes)} tensors per rank, {count * e / 2**20:.1f} MiB per rank")
+    del flat_in, bufs, flat
+    torch.cuda.empty_cache()
+
+
+def test_bucket8_rank_major_multi_out_of_place():
+    """The rank-major multi-tensor kernel with separate send and recv
+    allocations per tensor (fp16, 8 ranks, 140 MiB per rank), tiny tensors
+    among large ones: against the oracle."""
+    n, dtype = 8, "f16"
+    sizes = [1, 7, 70_000_000, 3, 4095, 1_500_001, 8, 1_900_000, 5]
+    assert sum(sizes) * 2 > 128 << 20
+    send, recv, exp = _multi_case(n, sizes, dtype, "sum", seed=78)
+    with ar.Comm(n, 0) as comm:
+        ar.ar_all_reduce_multi(comm, _ptrs(send), _ptrs(recv), sizes, dtype, "sum")
+        torch.cuda.synchronize()
+    _check_multi(recv, exp, dtype, "rank-major multi out of place")
+    for row in send + recv:
+        for b in row:
+            assert b.guards_ok()
+    del send, recv
+    torch.cuda.empty_cache()
+
+
 def _multi_case(n, sizes, dtype, op, seed):
     """Send tensors filled from a seeded flat bucket, empty recv tensors, and
     the oracle's flat-bucket result."""
