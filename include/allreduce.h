@@ -215,7 +215,10 @@ ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[], void* co
  * tensor in place on every rank takes n pointers, otherwise 2n: e.g. about
  * 40 in-place tensors per launch at 8 ranks, 6 at 64). Tensors whose rank
  * pointers all sit at the same offset from a 16-byte boundary are read and
- * written in 16-byte vectors; others element by element. No workspace. */
+ * written in 16-byte vectors; others element by element. When the pointers
+ * also share their offset from a 128-byte line (views at one offset into
+ * per-rank buckets), the vectors start on the tensor's first whole line,
+ * which keeps every wave's access to whole lines. No workspace. */
 ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const void* const sendbufs[], void* const recvbufs[],
                                 const size_t counts[], ar_dtype_t dtype, ar_op_t op, ar_mode_t mode,
                                 hipStream_t stream);
