@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grad7b]
                     [--mode fused|stepwise|graph|tree|tree_stepwise]
                     [--collective all_reduce|reduce_scatter|all_gather|all_to_all]
-                    [--multi] [--no-cpu-baseline]
+                    [--multi] [--streaming] [--no-cpu-baseline]
     python bench.py --sweep            # 1 KiB..256 MiB per rank, every mode, alpha-beta fit
     python bench.py --copy-probe BYTES # a plain device copy (HBM counter calibration)
 
@@ -325,6 +325,9 @@ def main():
                          "count in and out (out of place)")
     ap.add_argument("--multi", action="store_true",
                     help="bucket64/bucket8: reduce the bucket as its mixed-size tensors with ar_all_reduce_multi")
+    ap.add_argument("--streaming", action="store_true",
+                    help="non-temporal loads and stores at every size in the one-launch calls "
+                         "(ar_comm_set_streaming); by default only beyond the 256 MB last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line, sweep 1 KiB .. 256 MiB per rank (8 ranks, fp32 SUM) in every "
@@ -358,6 +361,8 @@ def main():
     wl = {"bucket8": "bucket64"}.get(args.workload, args.workload)
     wl = wl if wl in synthetic.WORKLOAD_IDS else "sweep"
     comm = ar.Comm(n, 0)
+    if args.streaming:
+        ar.ar_comm_set_streaming(comm, True)
     stream = torch.cuda.current_stream()
     sizes = None
     coll = args.collective
@@ -373,6 +378,8 @@ def main():
             sys.exit(2)
         sizes = synthetic.bucket_sizes(count, ESIZE[dtype], 4096, 64 << 20, seed=5)
         desc += f"; as {len(sizes)} tensors per rank through ar_all_reduce_multi"
+    if args.streaming:
+        desc += "; streaming (non-temporal) access"
 
     s_bytes = count * ESIZE[dtype]
     # A call whose rank buffers fit in the last-level cache would be timed
@@ -478,7 +485,8 @@ def main():
     # move more and are reported against the same bytes, so modes compare.
     alg_bytes = (2 * n if coll in ("all_reduce", "all_to_all") else n + 1) * s_bytes
     achieved = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = None if args.multi else load_traffic(args.workload, args.mode, coll)
+    # counter summaries cover the default access rule and the flat call
+    traffic = None if args.multi or args.streaming else load_traffic(args.workload, args.mode, coll)
     result = {
         "metric": METRIC,
         "value": round(algbw, 3),
@@ -498,6 +506,7 @@ def main():
         "config": {"workload": desc, "nranks": n, "count_per_rank": count, "bytes_per_rank": s_bytes, "op": op,
                    "mode": args.mode, "collective": coll,
                    "accumulate": "f32" if dtype in ("f16", "bf16") else dtype,
+                   "access": "streaming" if args.streaming else "non-temporal beyond the last-level cache",
                    "parallelism": f"{n} virtual ranks on 1 GPU"},
         "busbw": round(busbw, 3),
         "hbm_gbps": round(achieved, 1),

@@ -52,7 +52,7 @@ MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph"
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",
     "ar_all_reduce", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi",
-    "ar_comm_set_step_timing", "ar_last_step_times_ms",
+    "ar_comm_set_step_timing", "ar_comm_set_streaming", "ar_last_step_times_ms",
     "ar_result_string", "ar_last_error",
 )
 
@@ -73,6 +73,7 @@ _lib.ar_all_to_all.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_
 _lib.ar_all_reduce_multi.argtypes = [_vp, _c_int, _ptr_array, _ptr_array, ctypes.POINTER(_c_size), _c_int, _c_int,
                                      _c_int, _vp]
 _lib.ar_comm_set_step_timing.argtypes = [_vp, _c_int]
+_lib.ar_comm_set_streaming.argtypes = [_vp, _c_int]
 _lib.ar_last_step_times_ms.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]
 _lib.ar_result_string.argtypes = [_c_int]
 _lib.ar_result_string.restype = ctypes.c_char_p
@@ -80,7 +81,7 @@ _lib.ar_last_error.argtypes = []
 _lib.ar_last_error.restype = ctypes.c_char_p
 for _name in ("ar_comm_create", "ar_comm_destroy", "ar_comm_set_workspace", "ar_all_reduce", "ar_reduce_scatter",
               "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi", "ar_comm_set_step_timing",
-              "ar_last_step_times_ms"):
+              "ar_comm_set_streaming", "ar_last_step_times_ms"):
     getattr(_lib, _name).restype = _c_int
 
 
@@ -259,6 +260,10 @@ def ar_all_reduce_multi(comm, sendbufs, recvbufs, counts, dtype, op, mode="fused
 
 def ar_comm_set_step_timing(comm, enable: bool):
     _check(_lib.ar_comm_set_step_timing(_h(comm), 1 if enable else 0), "ar_comm_set_step_timing")
+
+
+def ar_comm_set_streaming(comm, enable: bool):
+    _check(_lib.ar_comm_set_streaming(_h(comm), 1 if enable else 0), "ar_comm_set_streaming")
 
 
 def ar_last_step_times_ms(comm, cap: int = 2 * MAX_RANKS + 1):

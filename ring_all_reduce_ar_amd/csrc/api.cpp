@@ -28,6 +28,7 @@ struct ar_comm {
     size_t ws_bytes = 0;
     bool debug = false;
     bool step_timing = false;
+    bool streaming = false;  // non-temporal access in the one-launch calls whatever the footprint
     std::vector<hipEvent_t> events;  // step boundaries of the last timed call
     int last_steps = -1;
     // AR_MODE_RING_GRAPH: instantiated graphs keyed by call signature.
@@ -189,6 +190,10 @@ int grid_for(const ar_comm* comm, uint64_t units_per_row, int rows, int per_cu =
 constexpr uint64_t kLastLevelCacheBytes = uint64_t(256) << 20;
 
 bool use_nt(uint64_t footprint_bytes) { return footprint_bytes > kLastLevelCacheBytes; }
+
+// The access flavour of a one-launch call: non-temporal beyond the cache, or
+// always when the comm is set to streaming. Launch shapes follow `beyond`.
+bool nt_access(const ar_comm* comm, bool beyond) { return beyond || comm->streaming; }
 
 // Distinct bytes of the rank buffers: in-place ranks count once.
 uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t send_bytes, uint64_t recv_bytes)
@@ -394,6 +399,13 @@ AR_EXPORT ar_result_t ar_comm_set_step_timing(ar_comm_t comm, int enable)
     return AR_SUCCESS;
 }
 
+AR_EXPORT ar_result_t ar_comm_set_streaming(ar_comm_t comm, int enable)
+{
+    if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
+    comm->streaming = enable != 0;
+    return AR_SUCCESS;
+}
+
 AR_EXPORT ar_result_t ar_last_step_times_ms(ar_comm_t comm, float* out, int cap, int* nsteps)
 {
     if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
@@ -535,7 +547,7 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         // per rank or at 32+ ranks, 8 above (measured ±2-3% at 8 ranks)
         const int per_cu = (count * e <= (size_t(128) << 20) || n >= 32) ? 16 : 8;
         const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, per_cu);
-        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, count * e, count * e));
+        const bool nt = nt_access(comm, use_nt(footprint(n, sendbufs, recvbufs, count * e, count * e)));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -611,9 +623,11 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         a.count = count;
         a.q = q;
         a.n = n;
-        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
-        const bool rank_major = use_rank_major(bytes, n, vec, nt);
-        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n, rank_major ? 16 : fused_per_cu(bytes, n, !nt));
+        const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
+        const bool nt = nt_access(comm, beyond);
+        const bool rank_major = use_rank_major(bytes, n, vec, beyond);
+        const int gx =
+            grid_for(comm, vec ? ceil_div(q, epv) : q, n, rank_major ? 16 : fused_per_cu(bytes, n, !beyond));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rank_major, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -703,12 +717,13 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.count = total;
         a.q = q;
         a.n = n;
-        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, sbytes, rbytes));
+        const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, sbytes, rbytes));
+        const bool nt = nt_access(comm, beyond);
         // Rank-major kernels at 5..8 ranks beyond the last-level cache: 16
         // workgroups per CU up to 4 GiB of input per rank, 8 above (+9 points
         // at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against the two-tile
         // kernels on the same buffers).
-        const bool rank_major = vec && nt && n >= 5 && n <= 8;
+        const bool rank_major = vec && beyond && n >= 5 && n <= 8;
         const int per_cu = rank_major ? (sbytes <= (size_t(4) << 30) ? 16 : 8) : (n <= 2 ? 4 : 8);
         const int gx_f = grid_for(comm, vec ? ceil_div(q, epv) : q, n, per_cu);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
@@ -774,12 +789,13 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
         fill_ptrs(a, n, sendbufs, recvbufs);
         a.total = blk;
         a.n = n;
-        const bool nt = use_nt(footprint(n, sendbufs, recvbufs, blk, rbytes));
+        const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, blk, rbytes));
+        const bool nt = nt_access(comm, beyond);
         // Rank-major copy at 5..8 ranks from 512 MiB of input per rank
         // (measured against the copy above at 8 ranks: +7.4 points at
         // 512 MiB, +1.0 at 1 GiB, +6.6 at 1.75 GB; 1-4 points slower at
         // 64-256 MiB).
-        const bool rank_major = vec && nt && n >= 5 && n <= 8 && blk >= (size_t(512) << 20);
+        const bool rank_major = vec && beyond && n >= 5 && n <= 8 && blk >= (size_t(512) << 20);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_gather(a, vec, nt, rank_major, gx_f, s);
             return err != hipSuccess ? err : tick(t);
@@ -858,8 +874,9 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
         // 4 workgroups per CU: each moves one block pair, a plain copy stream
         // (8 ranks x 256 MiB: 69.3% against 62.2% at 8)
         const int gx = grid_for(comm, units, n * n, 4);
+        const bool nt1 = nt_access(comm, nt);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_all_to_all(a, vec, nt, gx, s);
+            hipError_t err = ar::launch_all_to_all(a, vec, nt1, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -983,11 +1000,12 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
 
     uint64_t touched = 0;
     for (const Interval& x : iv) touched += x.hi - x.lo;
-    const bool nt = use_nt(touched);
+    const bool beyond = use_nt(touched);
+    const bool nt = nt_access(comm, beyond);
     // The rank-major kernel at 8 ranks, on the flat call's size rule (the
     // bucket's bytes per rank); its vector tiles are four kBlock-vector
     // quarters wide.
-    const bool rank_major = n == 8 && use_rank_major(total * e, n, true, nt);
+    const bool rank_major = n == 8 && use_rank_major(total * e, n, true, beyond);
     const uint64_t tile_vecs = rank_major ? ar::kMultiRankMajorTile : ar::kMultiVecTile;
 
     // Lays out tensors [t0, t1) of the plan as one table (pointer blocks,

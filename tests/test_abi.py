@@ -63,6 +63,7 @@ def test_null_comm_is_rejected_without_a_device():
     assert lib.ar_all_gather(None, arr, arr, 16, 0, 0, None) == ar.AR_ERR_INVALID_ARGUMENT
     assert lib.ar_comm_set_workspace(None, None, 0) == ar.AR_ERR_INVALID_ARGUMENT
     assert lib.ar_comm_set_step_timing(None, 1) == ar.AR_ERR_INVALID_ARGUMENT
+    assert lib.ar_comm_set_streaming(None, 1) == ar.AR_ERR_INVALID_ARGUMENT
     assert lib.ar_comm_destroy(None) == ar.AR_SUCCESS
     assert lib.ar_comm_nranks(None) == -1
 
