@@ -316,6 +316,40 @@ def pin_avg_pow2(o):
         assert same_bits(a, (s * np.float32(1.0 / n)).astype(np.float32)), n
 
 
+def pin_avg_divide(o):
+    """AVG is the finished sum divided once by N ("sum, then divide by N":
+    mhpq.cn article, section 2.1; geek-doc page "训练梯度同步与集合通信",
+    section 三), as one correctly rounded fp32 division, at any N. IEEE 754
+    division in numpy (np.float32 / np.float32) is the library routine:
+      fp32:      AVG == SUM / N, bit for bit;
+      fp16/bf16: the fp32 sum of the exactly widened inputs (the oracle's
+                 fp32 SUM of those fp32 values, whose order the ring-order
+                 golden pins) divided by N in fp32, then rounded once to the
+                 storage type by numpy (fp16) or torch (bf16), equals AVG.
+    Non-powers of two are where a reciprocal multiply, x * (1/N), differs
+    from x / N (power-of-two N are exact both ways)."""
+    rng = np.random.default_rng(23)
+    for n in (3, 5, 6, 7, 9, 63):
+        for dt in ("f32", "f16", "bf16"):
+            xs = random_inputs(rng, n, 2048, dt, "sum")
+            avg = o.fold_all_reduce(xs, dt, "avg")[0]
+            wide = [to_f64(a, dt).astype(np.float32) for a in xs]  # exact: every fp16/bf16 is an fp32
+            s32 = o.fold_all_reduce(wide, "f32", "sum")[0]
+            with np.errstate(over="ignore", under="ignore"):
+                q = (s32 / np.float32(n)).astype(np.float32)
+            if dt == "f32":
+                exp = q
+            elif dt == "f16":
+                with np.errstate(over="ignore"):
+                    exp = q.astype(np.float16)
+            else:
+                exp = torch.from_numpy(q.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert same_bits(avg, exp), (n, dt, int(np.sum(bits(avg) != bits(exp))))
+            ring = [a.copy() for a in xs]
+            o.ring_all_reduce(ring, dt, "avg")
+            assert same_bits(ring[0], exp), (n, dt, "ring form")
+
+
 def pin_prod_bound(o):
     """fp32 PROD against the exact product of the fp32 inputs (fractions): the
     relative error of N-1 rounded products is within gamma_{N-1}."""
@@ -523,7 +557,7 @@ def pin_tree(o):
 ALL_PINS = [
     pin_worked_example, pin_bytes_sent_page, pin_bytes_closed_form, pin_partition_torch_chunk,
     pin_ring_order, pin_fp32_accumulate, pin_forms_agree, pin_int_brute_force, pin_fp_maxmin,
-    pin_sum_error_bound, pin_avg_pow2, pin_prod_bound, pin_prod_double_rounding, pin_f16_conversions,
+    pin_sum_error_bound, pin_avg_pow2, pin_avg_divide, pin_prod_bound, pin_prod_double_rounding, pin_f16_conversions,
     pin_bf16_conversions,
     pin_rs_ag_equals_ar, pin_all_gather_concat, pin_elements_match, pin_all_to_all,
     pin_tree,

@@ -29,6 +29,7 @@ MUTANTS = [
     ("int_sum_sign", "r.u = local.u + incoming.u;", "r.u = local.u - incoming.u;"),
     ("avg_not_divided", "a.f = a.f / (float)n;", "a.f = a.f;"),
     ("avg_multiplies_reciprocal", "a.f = a.f / (float)n;", "a.f = a.f * (1.0f / (float)(3 * n));"),
+    ("avg_reciprocal_of_n", "a.f = a.f / (float)n;", "a.f = a.f * (1.0f / (float)n);"),
     ("int_avg_floor", "a.u = (uint32_t)((int32_t)a.u / (int32_t)n);",
      "a.u = (uint32_t)(int32_t)floor((double)(int32_t)a.u / (double)n);"),
     ("max_zero_sign", "return (signbit(a) && signbit(b)) ? -0.0f : 0.0f;",
