@@ -39,8 +39,9 @@ Reported (one JSON line):
   copy_ceiling a plain 1 GiB device copy timed in the same process: the
                practical read-once write-once rate of this machine, and the
                call's rate over it
-  cpu_baseline the CPU oracle (one thread) on the workload, or a window of it,
-               in the same unit
+  cpu_baseline the CPU oracle on the workload, or a window of it, in the same
+               unit: the literal ring on the host's threads (OMP_NUM_THREADS,
+               else the affinity mask), and beside it the per-element fold
 """
 from __future__ import annotations
 
@@ -51,6 +52,8 @@ import os
 import re
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "all-reduce algbw/busbw GB/s and % HBM peak, N=8 ranks, 64 MiB–14 GB msgs"
@@ -164,14 +167,38 @@ def load_traffic(workload: str, mode: str, collective: str = "all_reduce"):
     return float(t.group(1))
 
 
+def cpu_threads() -> int:
+    """Host threads for the CPU oracle: OMP_NUM_THREADS when set (the host's
+    CPU share for this job), else every core in this process's affinity mask."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    t = int(env) if env.isdigit() and int(env) > 0 else len(os.sched_getaffinity(0))
+    return max(1, min(t, 256))
+
+
+def _time_repeated(fn, min_seconds):
+    """Calls fn until min_seconds have passed; returns (calls, seconds)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return reps, dt
+
+
 def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "all_reduce", count: int = 0):
-    """The oracle on a sample of the same workload, timed on one host
-    thread: the literal ring for all-reduce, the oracle's reduce-scatter,
-    all-gather or all-to-all otherwise. The sample is the workload itself
-    when its `count` elements per rank fit in 2^CPU_WINDOW_LOG2, else a
-    window of that many elements per rank, seeded the same way; a sample
-    that runs in under CPU_MIN_SECONDS is repeated until that much time has
-    passed. algbw convention as the GPU line."""
+    """The oracle on a sample of the same workload, timed on the host's cores.
+    All-reduce: the literal ring with every ring half-step split over
+    (rank x piece) on T threads and a barrier between half-steps (the ranks
+    of the handbook's ring step together: "集合通信原语", section 环形 all-reduce
+    与通信量) is `value`; the per-element fold on the same T threads is timed
+    beside it (`fold`). The other collectives run the oracle's serial
+    reduce-scatter, all-gather or all-to-all on one thread. The sample is the
+    workload itself when its `count` elements per rank fit in
+    2^CPU_WINDOW_LOG2, else a window of that many elements per rank, seeded
+    the same way; a sample that runs in under CPU_MIN_SECONDS is repeated
+    until that much time has passed. algbw convention as the GPU line."""
     import oracle
     import synthetic
     window = 1 << CPU_WINDOW_LOG2
@@ -182,33 +209,34 @@ def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "a
     import torch
     dev = "cuda" if torch.cuda.is_available() else "cpu"
     xs = [synthetic.to_numpy(t) for t in synthetic.rank_inputs(wl, nranks, in_count, dtype, device=dev, op=op)]
-    what = {"all_reduce": "literal ring (N-1 reduce-scatter + N-1 all-gather steps)", "reduce_scatter": "reduce-scatter",
-            "all_gather": "all-gather"}.get(coll, "all-to-all")
-
-    def once():
-        if coll == "all_reduce":
-            oracle.ring_all_reduce(xs, dtype, op)
-        elif coll == "reduce_scatter":
-            oracle.reduce_scatter(xs, dtype, op)
-        elif coll == "all_gather":
-            oracle.all_gather(xs, dtype)
-        else:
-            oracle.all_to_all(xs, dtype)
-
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        once()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= CPU_MIN_SECONDS:
-            break
+    threads = cpu_threads() if coll == "all_reduce" else 1
+    what = {"all_reduce": f"literal ring (N-1 reduce-scatter + N-1 all-gather steps, each half-step over "
+                          f"rank x piece on {threads} threads, a barrier between half-steps)",
+            "reduce_scatter": "reduce-scatter, single thread", "all_gather": "all-gather, single thread"}.get(
+        coll, "all-to-all, single thread")
+    if coll == "all_reduce":
+        bufs = [a.copy() for a in xs]
+        reps, dt = _time_repeated(lambda: oracle.ring_all_reduce_threads(bufs, dtype, op, threads), CPU_MIN_SECONDS)
+        outs = [np.empty_like(a) for a in xs]
+        freps, fdt = _time_repeated(lambda: oracle.fold_all_reduce_threads(xs, dtype, op, threads, out=outs),
+                                    CPU_MIN_SECONDS)
+        del bufs, outs
+    else:
+        fn = {"reduce_scatter": lambda: oracle.reduce_scatter(xs, dtype, op),
+              "all_gather": lambda: oracle.all_gather(xs, dtype)}.get(coll, lambda: oracle.all_to_all(xs, dtype))
+        reps, dt = _time_repeated(fn, CPU_MIN_SECONDS)
     s_bytes = sample * ESIZE[dtype]
     part = "the whole workload" if sample == count else f"a window of the {count}-element workload" if count else "a window"
-    return {"value": s_bytes * reps / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nranks} ranks x {sample} {dtype} elements per rank ({s_bytes / 2**20:.1f} MiB; {part}), "
-                      f"{what}, {op}, single thread" + (f", {reps} calls" if reps > 1 else ""),
-            "seconds": dt}
+    out = {"value": s_bytes * reps / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{nranks} ranks x {sample} {dtype} elements per rank ({s_bytes / 2**20:.1f} MiB; {part}), "
+                     f"{what}, {op}" + (f", {reps} calls" if reps > 1 else ""),
+           "seconds": dt}
+    if coll == "all_reduce":
+        out["fold"] = {"value": s_bytes * freps / fdt / 1e9, "unit": "GB/s", "cores": threads, "seconds": fdt,
+                       "calls": freps,
+                       "form": "per-element fold (acc = x_c[i]; acc = x_{c+k}[i] (+) acc), contiguous element "
+                               "ranges on the same threads"}
+    return out
 
 
 def time_copy(torch, ar, nbytes: int, steps: int, warmup: int):

@@ -28,6 +28,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ring_oracle.c")
+# The default library is built from the threaded timing harness, which
+# includes ring_oracle.c: it holds the serial checker and the threaded forms.
+_SRC_THREADS = os.path.join(_HERE, "ring_oracle_threads.c")
 _LIB = os.path.join(_HERE, "liboracle_ar.so")
 
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i32": 3}
@@ -35,14 +38,17 @@ OPS = {"sum": 0, "avg": 1, "max": 2, "min": 3, "prod": 4}
 NP_DTYPE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "i32": np.int32}
 ELEM_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4}
 
-GCC_CMD = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+GCC_CMD = ["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off", "-fno-fast-math",
            "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm"]
 
 
-def build(src: str = _SRC, out: str = _LIB) -> str:
+def build(src: str = _SRC_THREADS, out: str = _LIB) -> str:
     """Compile the oracle with gcc (always recompiles). Returns the library path.
-    Each process compiles to its own temporary file and renames it into place,
-    so parallel test workers building at once do not race."""
+    The default source is the threaded harness (serial checker included); a
+    test may build a variant of ring_oracle.c alone, which then lacks the
+    threaded entry points. Each process compiles to its own temporary file
+    and renames it into place, so parallel test workers building at once do
+    not race."""
     tmp = f"{out}.tmp{os.getpid():x}"
     cmd = [tmp if a == _LIB else src if a == _SRC else a for a in GCC_CMD]
     subprocess.run(cmd, check=True)
@@ -70,6 +76,10 @@ class Oracle:
         for name in ("orc_f32_to_f16", "orc_f16_to_f32", "orc_f32_to_bf16", "orc_bf16_to_f32"):
             getattr(lib, name).argtypes = [vp, vp, u64]
             getattr(lib, name).restype = None
+        self.threaded = hasattr(lib, "orc_ring_all_reduce_threads")
+        if self.threaded:
+            lib.orc_ring_all_reduce_threads.argtypes = [i32, u64, i32, i32, pp, pu64, i32]
+            lib.orc_fold_all_reduce_threads.argtypes = [i32, u64, i32, i32, pp, pp, i32]
         self.lib = lib
         self.path = path
 
@@ -83,6 +93,32 @@ class Oracle:
         sent = (ctypes.c_uint64 * n)()
         _rc(self.lib.orc_ring_all_reduce(n, count, DTYPES[dtype], OPS[op], _ptrs(bufs), sent), "ring_all_reduce")
         return [int(s) for s in sent]
+
+    def ring_all_reduce_threads(self, bufs, dtype: str, op: str, nthreads: int):
+        """ring_all_reduce on ``nthreads`` host threads: each half-step of the
+        ring (all ranks send; all ranks combine or copy) split over
+        (rank x piece) items, a barrier between half-steps. Same bytes and
+        byte counts as the serial form. Returns the bytes each rank sent."""
+        n = len(bufs)
+        count = bufs[0].size
+        _check_bufs(bufs, dtype, count)
+        sent = (ctypes.c_uint64 * n)()
+        _rc(self.lib.orc_ring_all_reduce_threads(n, count, DTYPES[dtype], OPS[op], _ptrs(bufs), sent, nthreads),
+            "ring_all_reduce_threads")
+        return [int(s) for s in sent]
+
+    def fold_all_reduce_threads(self, inputs, dtype: str, op: str, nthreads: int, out=None):
+        """fold_all_reduce on ``nthreads`` host threads over element ranges.
+        ``out`` (one array per rank, may be ``inputs``) receives the result;
+        new arrays are returned when it is None."""
+        n = len(inputs)
+        count = inputs[0].size
+        _check_bufs(inputs, dtype, count)
+        outs = out if out is not None else [np.empty(count, dtype=NP_DTYPE[dtype]) for _ in range(n)]
+        _check_bufs(outs, dtype, count)
+        _rc(self.lib.orc_fold_all_reduce_threads(n, count, DTYPES[dtype], OPS[op], _ptrs(inputs), _ptrs(outs),
+                                                 nthreads), "fold_all_reduce_threads")
+        return outs
 
     def fold_all_reduce(self, inputs, dtype: str, op: str):
         """Per-element-fold all-reduce. Returns one new output array per rank."""
@@ -204,7 +240,8 @@ def get() -> Oracle:
     """The default oracle build (compiled on first use if missing or stale)."""
     global _default
     if _default is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(_SRC),
+                                                                     os.path.getmtime(_SRC_THREADS)):
             build()
         _default = Oracle(_LIB)
     return _default
@@ -216,6 +253,14 @@ def ring_all_reduce(bufs, dtype, op):
 
 def fold_all_reduce(inputs, dtype, op):
     return get().fold_all_reduce(inputs, dtype, op)
+
+
+def ring_all_reduce_threads(bufs, dtype, op, nthreads):
+    return get().ring_all_reduce_threads(bufs, dtype, op, nthreads)
+
+
+def fold_all_reduce_threads(inputs, dtype, op, nthreads, out=None):
+    return get().fold_all_reduce_threads(inputs, dtype, op, nthreads, out)
 
 
 def all_reduce_elements(vals, idx, count, dtype, op):

@@ -5,11 +5,23 @@ import bench
 
 def test_cpu_baseline_takes_the_whole_workload_when_it_fits(monkeypatch):
     monkeypatch.setattr(bench, "CPU_MIN_SECONDS", 0.0)
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
     r = bench.cpu_baseline(4, "f32", "sum", "sweep", "all_reduce", count=4096)
-    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s"
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
     assert "4 ranks x 4096 f32 elements per rank" in r["sample"]
     assert "the whole workload" in r["sample"]
     assert r["value"] > 0 and r["seconds"] > 0
+    # the all-reduce runs on the host's threads, and the fold is timed beside it
+    assert r["cores"] == 3 and "on 3 threads" in r["sample"]
+    assert r["fold"]["cores"] == 3 and r["fold"]["value"] > 0
+
+
+def test_cpu_threads_follow_the_host_share(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "16")
+    assert bench.cpu_threads() == 16
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    import os
+    assert bench.cpu_threads() == len(os.sched_getaffinity(0))
 
 
 def test_cpu_baseline_windows_a_larger_workload(monkeypatch):
@@ -19,6 +31,7 @@ def test_cpu_baseline_windows_a_larger_workload(monkeypatch):
     assert "8 ranks x 1024 f16 elements per rank" in r["sample"]
     assert "a window of the 7000000000-element workload" in r["sample"]
     assert "reduce-scatter" in r["sample"]
+    assert r["cores"] == 1 and "fold" not in r
 
 
 def test_cpu_baseline_repeats_a_short_sample(monkeypatch):
