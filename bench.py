@@ -65,6 +65,8 @@ CSRC = os.path.join(ROOT, "ring_all_reduce_ar_amd", "csrc")
 
 # workload name -> (nranks, count, dtype, op, description)
 WORKLOADS = {
+    "small": (4, 4096, "f32", "sum",
+              "small: 4 virtual ranks x 4096 fp32, uniform[-1,1), SUM, in place (the handbook's 4-rank ring shape)"),
     "grad7b": (8, 7_000_000_000, "f16", "avg",
                "grad7b: 8 virtual ranks x 7e9 fp16 gradient (14 GB per rank), N(0,1e-3^2) with 1% N(0,1) "
                "outliers, AVG with fp32 accumulation, in place"),
@@ -239,6 +241,74 @@ def cpu_baseline(nranks: int, dtype: str, op: str, workload: str, coll: str = "a
     return out
 
 
+def sig(x: float, digits: int = 6) -> float:
+    """x rounded to `digits` significant digits (the line's rates span
+    0.001 to 10^4 GB/s)."""
+    return float(f"{x:.{digits}g}")
+
+
+def time_steps(torch, stream, step, k: int, warmup: int, rotate: bool = True, per_step_events: bool = False):
+    """Warm up, then time exactly k calls of step(i) on `stream`. The timed
+    pass brackets the k calls with two events only: an event recorded between
+    kernels costs the stream a few microseconds, which shows at short calls.
+    With per_step_events an event follows every call instead. Returns
+    (ms per call, None) or (None, [ms of each call])."""
+    for i in range(warmup):
+        step(i if rotate else 0)
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1 if per_step_events else 2)]
+    torch.cuda.synchronize()
+    events[0].record(stream)
+    for i in range(k):
+        step(i if rotate else 0)
+        if per_step_events:
+            events[i + 1].record(stream)
+    if not per_step_events:
+        events[1].record(stream)
+    torch.cuda.synchronize()
+    if not per_step_events:
+        return events[0].elapsed_time(events[1]) / k, None
+    return None, [events[i].elapsed_time(events[i + 1]) for i in range(k)]
+
+
+# The metric's range at 8 ranks below the headline size, timed after it in
+# the default run: (workload, steps). Each point allocates its rank buffers
+# twice and reports the second allocation (the first beside it), as the
+# headline does; bucket25 rotates buffer sets so every call reads HBM.
+RANGE_POINTS = (("sweep64m", 100), ("sweep256m", 50), ("bucket25", 200))
+
+
+def range_point(torch, ar, synthetic, name: str, steps: int, warmup: int, copy_gbps: float):
+    """One fused in-place all-reduce workload of the metric's range, timed as
+    the headline is (two allocations, rotation below the last-level cache)."""
+    n, count, dtype, op, desc = WORKLOADS[name]
+    wl = name if name in synthetic.WORKLOAD_IDS else "sweep"
+    s_bytes = count * ESIZE[dtype]
+    sets = 1 if n * s_bytes > LLC_BYTES else -(-ROTATE_BYTES // (n * s_bytes))
+    stream = torch.cuda.current_stream()
+    times = []
+    with ar.Comm(n, 0) as comm:
+        for _ in range(2):
+            bufsets = [synthetic.rank_inputs(wl, n, count, dtype, device="cuda", op=op, salt=k) for k in range(sets)]
+            ptrsets = [[b.data_ptr() for b in bufs] for bufs in bufsets]
+
+            def step(i):
+                p = ptrsets[i % sets]
+                ar.ar_all_reduce(comm, p, p, count, dtype, op, "fused", stream)
+
+            times.append(time_steps(torch, stream, step, steps, warmup)[0])
+            del bufsets, ptrsets
+            torch.cuda.empty_cache()
+    ms = times[1]
+    alg = 2 * n * s_bytes / (ms * 1e-3) / 1e9
+    algbw = s_bytes / (ms * 1e-3) / 1e9
+    return {"workload": desc, "nranks": n, "bytes_per_rank": s_bytes, "dtype": dtype, "op": op, "mode": "fused",
+            "steps": steps, "rotating_buffer_sets": sets, "ms_per_step": sig(ms),
+            "first_allocation_ms_per_step": sig(times[0]), "algbw_gbps": sig(algbw),
+            "busbw_gbps": sig(algbw * 2 * (n - 1) / n), "hbm_gbps": sig(alg),
+            "hbm_frac": sig(alg / HBM_PEAK_GBPS), "achieved_over_copy": sig(alg / copy_gbps)}
+
+
 def time_copy(torch, ar, nbytes: int, steps: int, warmup: int):
     """Plain device copy of `nbytes` (a one-rank all-gather: 16-byte loads
     and stores, src read once, dst written once). Returns (ms per copy,
@@ -345,7 +415,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="grad7b", choices=sorted(WORKLOADS))
-    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise", "graph", "tree", "tree_stepwise"])
+    ap.add_argument("--mode", default=None, choices=["fused", "stepwise", "graph", "tree", "tree_stepwise"],
+                    help="default: stepwise for --workload small (the ring whose per-step cost it measures), "
+                         "fused otherwise")
+    ap.add_argument("--no-range", action="store_true",
+                    help="skip the metric-range block (8 x 64 MiB, 8 x 256 MiB, the cold 25 MiB bucket) that "
+                         "follows the default headline line")
     ap.add_argument("--collective", default="all_reduce",
                     choices=["all_reduce", "reduce_scatter", "all_gather", "all_to_all"],
                     help="the collective to time on the workload's rank buffers: reduce_scatter takes count "
@@ -385,6 +460,8 @@ def main():
     if args.sweep:
         sweep(args, torch, ar, synthetic)
         return
+    if args.mode is None:
+        args.mode = "stepwise" if args.workload == "small" else "fused"
     n, count, dtype, op, desc = WORKLOADS[args.workload]
     wl = {"bucket8": "bucket64"}.get(args.workload, args.workload)
     wl = wl if wl in synthetic.WORKLOAD_IDS else "sweep"
@@ -463,43 +540,35 @@ def main():
                 ar.ar_all_reduce_multi(comm, rows, rows, sizes, dtype, op, "fused", stream)
 
         def run(k, rotate, per_step_events=False):
-            # The timed pass brackets the K steps with two events only: an
-            # event recorded between kernels costs the stream a few
-            # microseconds, which shows at short calls. The per-step times
-            # come from a separate pass with an event after every step.
-            for i in range(args.warmup):
-                step(i if rotate else 0)
-            torch.cuda.synchronize()
-            events = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1 if per_step_events else 2)]
-            torch.cuda.synchronize()
-            events[0].record(stream)
-            for i in range(k):
-                step(i if rotate else 0)
-                if per_step_events:
-                    events[i + 1].record(stream)
-            if not per_step_events:
-                events[1].record(stream)
-            torch.cuda.synchronize()
-            if not per_step_events:
-                return events[0].elapsed_time(events[1]) / k, None
-            return None, [events[i].elapsed_time(events[i + 1]) for i in range(k)]
+            return time_steps(torch, stream, step, k, args.warmup, rotate, per_step_events)
 
         print(f"[bench] timing {args.warmup} warmup + {args.steps} steps", file=sys.stderr, flush=True)
         ms_ = run(args.steps, True)[0]
         per_step = run(args.steps, True, per_step_events=True)[1]
         warm = run(args.steps, False)[0] if measure_warm and sets > 1 else None
+        ring_steps = None
+        if measure_warm and args.mode in ("stepwise", "tree_stepwise"):
+            # events between the ring's launches (ar_comm_set_step_timing):
+            # each launch's device time, over K calls
+            ar.ar_comm_set_step_timing(comm, True)
+            calls = []
+            for i in range(args.steps):
+                step(i)
+                calls.append(ar.ar_last_step_times_ms(comm))
+            ar.ar_comm_set_step_timing(comm, False)
+            ring_steps = calls
         ar.ar_comm_set_workspace(comm, None)
         del bufsets, ptrsets, outsets, outptrs, ws
         torch.cuda.empty_cache()
-        return ms_, per_step, warm
+        return ms_, per_step, warm, ring_steps
 
     # The first allocation of the rank buffers in a fresh process measured up
     # to ~9% slower on MI355X than the same buffers allocated again after a
     # free (same virtual addresses, different physical backing). Both passes
     # are timed; the second is the steady state a long-running job sees and
     # is the reported value; the first is reported beside it.
-    first_ms, _, _ = timed_pass(False)
-    ms, per_step, warm_ms = timed_pass(True)
+    first_ms = timed_pass(False)[0]
+    ms, per_step, warm_ms, ring_steps = timed_pass(True)
     per_step.sort()
 
     # nccl-tests conventions: algbw = S / T with S the per-rank buffer of
@@ -517,15 +586,15 @@ def main():
     traffic = None if args.multi or args.streaming else load_traffic(args.workload, args.mode, coll)
     result = {
         "metric": METRIC,
-        "value": round(algbw, 3),
+        "value": sig(algbw),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "first_allocation_ms_per_step": round(first_ms, 4),
-        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
-                    "max": round(per_step[-1], 4)},
+        "ms_per_step": sig(ms),
+        "first_allocation_ms_per_step": sig(first_ms),
+        "step_ms": {"median": sig(per_step[len(per_step) // 2]), "min": sig(per_step[0]),
+                    "max": sig(per_step[-1])},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -536,29 +605,52 @@ def main():
                    "accumulate": "f32" if dtype in ("f16", "bf16") else dtype,
                    "access": "streaming" if args.streaming else "non-temporal beyond the last-level cache",
                    "parallelism": f"{n} virtual ranks on 1 GPU"},
-        "busbw": round(busbw, 3),
-        "hbm_gbps": round(achieved, 1),
-        "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "busbw": sig(busbw),
+        "hbm_gbps": sig(achieved),
+        "hbm_frac": sig(achieved / HBM_PEAK_GBPS),
+        "roofline": {"bound": "hbm", "achieved": sig(achieved), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": sig(achieved / HBM_PEAK_GBPS),
                      "traffic": traffic},
     }
     if coll == "all_reduce" and args.mode in ("stepwise", "graph"):
         moved = ring_moved_bytes(n, count, dtype)
-        result["moved"] = {"bytes": moved, "gbps": round(moved / (ms * 1e-3) / 1e9, 1),
-                           "frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        result["moved"] = {"bytes": moved, "gbps": sig(moved / (ms * 1e-3) / 1e9),
+                           "frac": sig(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS),
                            "note": "bytes the 2(N-1) ring steps read and write, over the call's time"}
     if sets > 1:
         result["config"]["rotating_buffer_sets"] = sets
-        result["cache_resident"] = {"ms_per_step": round(warm_ms, 4),
-                                    "effective_gbps": round(alg_bytes / (warm_ms * 1e-3) / 1e9, 1),
+        result["cache_resident"] = {"ms_per_step": sig(warm_ms),
+                                    "effective_gbps": sig(alg_bytes / (warm_ms * 1e-3) / 1e9),
                                     "note": "one buffer set called back to back; served from the last-level cache"}
     # A plain 1 GiB device copy in the same process: the practical ceiling of
     # a read-once write-once stream on this machine, reported beside the roofline.
     cms, cgbps = time_copy(torch, ar, COPY_CEILING_BYTES, 20, 3)
-    result["copy_ceiling"] = {"bytes": COPY_CEILING_BYTES, "ms": round(cms, 4), "hbm_gbps": round(cgbps, 1),
-                              "hbm_frac": round(cgbps / HBM_PEAK_GBPS, 4),
-                              "achieved_over_copy": round(achieved / cgbps, 4)}
+    result["copy_ceiling"] = {"bytes": COPY_CEILING_BYTES, "ms": sig(cms), "hbm_gbps": sig(cgbps),
+                              "hbm_frac": sig(cgbps / HBM_PEAK_GBPS),
+                              "achieved_over_copy": sig(achieved / cgbps)}
+    if ring_steps:
+        # Per-launch device times of the ring (the alpha-beta model's steps:
+        # geek-doc page "训练梯度同步与集合通信", section 四; handbook
+        # "集合通信原语", section α-β 模型). At a few KiB per rank a step
+        # moves almost nothing, so its time is the per-step alpha on the
+        # device; the call time over its launches is what a caller pays per
+        # step, host enqueue included.
+        launches = len(ring_steps[0])
+        med = [sorted(c[j] for c in ring_steps)[len(ring_steps) // 2] for j in range(launches)]
+        result["ring_steps"] = {
+            "launches": launches, "step_us_median": [sig(t * 1e3) for t in med],
+            "alpha_device_us": sig(sum(med) / launches * 1e3),
+            "alpha_call_us": sig(ms * 1e3 / launches),
+            "note": "step_us: events between the launches of one call (median over K calls); alpha_device_us "
+                    "their mean; alpha_call_us: ms_per_step over the launches (host enqueue included)"}
+    if (args.workload == "grad7b" and coll == "all_reduce" and args.mode == "fused" and not args.multi
+            and not args.streaming and not args.no_range):
+        # the metric's range below the headline: 8 ranks x 64 MiB, 256 MiB and
+        # the cold 25 MiB DDP bucket, against the same copy ceiling
+        result["range"] = []
+        for name, k in RANGE_POINTS:
+            print(f"[bench] range point {name}", file=sys.stderr, flush=True)
+            result["range"].append(range_point(torch, ar, synthetic, name, k, 10, cgbps))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(n, dtype, op, args.workload, coll, count)

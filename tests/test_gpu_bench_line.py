@@ -39,7 +39,7 @@ def check_common(j, steps, warmup, workload):
     assert S == cfg["count_per_rank"] * bench.ESIZE[j["dtype"]]
     T = j["ms_per_step"] * 1e-3
     assert T > 0
-    # the printed figures are rounded (ms to 4 decimals, rates to 3 or 1)
+    # the printed figures are rounded to 6 significant digits
     assert j["value"] == pytest.approx(S / T / 1e9, rel=2e-3)
     assert j["busbw"] == pytest.approx(j["value"] * 2 * (n - 1) / n, rel=1e-4)
     assert j["hbm_gbps"] == pytest.approx(2 * n * S / T / 1e9, rel=2e-3)
@@ -75,3 +75,33 @@ def test_bench_line_multi_tensor_bucket():
     check_common(j, 3, 1, "bucket8")
     assert "ar_all_reduce_multi" in j["config"]["workload"]
     assert j["roofline"]["traffic"] is None  # counters are summarized for the flat call only
+
+
+def test_bench_line_small_stepwise_steps():
+    """The handbook's 4-rank shape defaults to the stepwise ring and reports
+    each launch's device time and the per-step alpha."""
+    j = run_bench("--workload", "small", "--steps", "5", "--warmup", "2", "--no-cpu-baseline")
+    n, S, T = check_common(j, 5, 2, "small")
+    assert n == 4 and S == 4096 * 4 and j["config"]["mode"] == "stepwise"
+    rs = j["ring_steps"]
+    assert rs["launches"] == 2 * (n - 1) and len(rs["step_us_median"]) == 2 * (n - 1)
+    assert all(t > 0 for t in rs["step_us_median"])
+    assert rs["alpha_device_us"] == pytest.approx(sum(rs["step_us_median"]) / (2 * (n - 1)), rel=1e-2, abs=0.01)
+    assert rs["alpha_call_us"] == pytest.approx(j["ms_per_step"] * 1e3 / (2 * (n - 1)), rel=1e-3, abs=1e-3)
+
+
+def test_range_point_fields():
+    """One point of the metric-range block the default line carries."""
+    import torch
+
+    import ring_all_reduce_ar_amd as ar
+    import synthetic
+    p = bench.range_point(torch, ar, synthetic, "bucket25", 3, 1, copy_gbps=4000.0)
+    n, S = p["nranks"], p["bytes_per_rank"]
+    assert n == 8 and S == 6_553_600 * 4 and p["rotating_buffer_sets"] >= 6
+    T = p["ms_per_step"] * 1e-3
+    assert p["algbw_gbps"] == pytest.approx(S / T / 1e9, rel=2e-3)
+    assert p["hbm_gbps"] == pytest.approx(2 * n * S / T / 1e9, rel=2e-3)
+    assert p["hbm_frac"] == pytest.approx(p["hbm_gbps"] / 8000.0, abs=1e-4)
+    assert p["achieved_over_copy"] == pytest.approx(p["hbm_gbps"] / 4000.0, rel=1e-3)
+    assert p["first_allocation_ms_per_step"] > 0

@@ -36,21 +36,49 @@ def gather(bufs, idx):
     return synthetic.to_numpy(vals.view(-1)).reshape(vals.shape)
 
 
-def check_sampled(comm, bufs, dtype, op, mode, seed=0):
-    """In-place all-reduce of bufs, checked at sampled elements and for
-    identical ranks."""
+def window_inputs(bufs, lo, hi):
+    """Every rank's elements [lo, hi) as a host array of shape (hi - lo, n)."""
+    vals = torch.stack([b[lo:hi] for b in bufs], dim=1).contiguous()
+    return synthetic.to_numpy(vals.view(-1)).reshape(vals.shape)
+
+
+def check_sampled(comm, bufs, dtype, op, mode, seed=0, windows=()):
+    """In-place all-reduce of bufs, checked at sampled elements, on every
+    element of the contiguous windows [lo, hi) given, and for identical
+    ranks. The oracle computes each checked element from host copies of its
+    inputs taken before the call."""
     n, count = len(bufs), bufs[0].numel()
     idx = sample_indices(n, count, np.random.default_rng(seed))
     before = gather(bufs, idx)
     exp = oracle.all_reduce_elements(before, idx, count, dtype, op)
+    win_exp = []
+    for lo, hi in windows:
+        assert 0 <= lo < hi <= count
+        win_exp.append(oracle.all_reduce_elements(window_inputs(bufs, lo, hi), np.arange(lo, hi, dtype=np.uint64),
+                                                  count, dtype, op))
     ptrs = [b.data_ptr() for b in bufs]
     ar.ar_all_reduce(comm, ptrs, ptrs, count, dtype, op, mode)
     torch.cuda.synchronize()
     after = gather(bufs, idx)
     for r in range(n):
         gu.assert_same(np.ascontiguousarray(after[:, r]), exp, dtype, f"{mode} {dtype} {op} rank {r} sampled")
+    for (lo, hi), w in zip(windows, win_exp):
+        for r in range(n):
+            gu.assert_same(synthetic.to_numpy(bufs[r][lo:hi]), w, dtype,
+                           f"{mode} {dtype} {op} rank {r} window [{lo}, {hi})")
     for r in range(1, n):
         assert torch.equal(bufs[r].view(torch.uint8), bufs[0].view(torch.uint8)), f"rank {r} differs from rank 0"
+
+
+def headline_windows(n, count, width=1 << 24):
+    """Four contiguous windows of `width` elements: the start, one straddling
+    the boundary between chunks 3 and 4, one straddling element 2^32 (where
+    32-bit element indices would wrap), and the end."""
+    q = -(-count // n)
+    mids = [n // 2 * q, 1 << 32]
+    out = [(0, width)] + [(m - width // 2, m + width // 2) for m in mids if width // 2 <= m <= count - width // 2]
+    out.append((count - width, count))
+    return out
 
 
 def free():
@@ -97,19 +125,29 @@ def test_sweep_sizes(mode, dtype):
     free()
 
 
+def test_headline_windows_cover_the_shape():
+    w = headline_windows(8, 7_000_000_000)
+    assert len(w) == 4 and all(hi - lo == 1 << 24 for lo, hi in w)
+    assert w[0][0] == 0 and w[-1][1] == 7_000_000_000
+    assert w[1][0] < 4 * 875_000_000 < w[1][1] and w[2][0] < 1 << 32 < w[2][1]
+
+
 def test_grad7b_fp16_avg():
     """8 ranks x 7e9 fp16 (14 GB each), N(0, 1e-3^2) with 1% N(0, 1)
     outliers, AVG with fp32 accumulation, in place: fused (the benchmark's
-    launch), then stepwise on fresh inputs with its 28 GB fp32 workspace."""
+    launch), then stepwise on fresh inputs with its 28 GB fp32 workspace.
+    Sampled elements plus four contiguous windows of 2^24 elements, compared
+    element by element."""
     n, count = 8, 7_000_000_000
+    wins = headline_windows(n, count)
     with ar.Comm(n, 0) as comm:
         bufs = synthetic.rank_inputs("grad7b", n, count, "f16", device="cuda")
-        check_sampled(comm, bufs, "f16", "avg", "fused", seed=4)
+        check_sampled(comm, bufs, "f16", "avg", "fused", seed=4, windows=wins)
         for r, b in enumerate(bufs):
             synthetic.gaussian(count, 1e-3, synthetic.generator("grad7b", r, "cuda", salt=1), torch.float16,
                                "cuda", outlier_frac=0.01, out=b)
         ws = gu.attach_workspace(comm, ar.AR_COLL_ALL_REDUCE, n, count, "f16", "stepwise")
-        check_sampled(comm, bufs, "f16", "avg", "stepwise", seed=5)
+        check_sampled(comm, bufs, "f16", "avg", "stepwise", seed=5, windows=wins)
         ar.ar_comm_set_workspace(comm, None)
         del ws
     del bufs
