@@ -55,6 +55,9 @@ extern "C" {
 
 #define AR_MAX_RANKS 64
 #define AR_MAX_TENSORS 65536
+/* Bytes of the library-owned device scratch array that ar_all_reduce_noalloc
+ * uses on each GPU (64 MiB). */
+#define AR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef struct ar_comm* ar_comm_t;
 
@@ -169,6 +172,30 @@ ar_result_t ar_comm_set_workspace(ar_comm_t comm, void* dev_ptr, size_t bytes);
  * element-wise kernels. The results are the same bits either way. */
 ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
                           ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
+
+/* Allocation-free all-reduce, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, results (bit for bit) and errors as
+ * ar_all_reduce, with these differences:
+ *  - the fp32 partial sums of the ring-stepwise and tree-stepwise fp16/bf16
+ *    paths live in a library-owned device array of AR_NOALLOC_SCRATCH_BYTES
+ *    on each GPU (set up by ar_comm_create, held until the process ends);
+ *    the comm's workspace is not used. A call that would need more, i.e.
+ *    ar_workspace_bytes(AR_COLL_ALL_REDUCE, ...) > AR_NOALLOC_SCRATCH_BYTES
+ *    (ring-stepwise fp16/bf16 beyond 16,777,216 elements per rank), is
+ *    INVALID_ARGUMENT;
+ *  - AR_MODE_RING_GRAPH is UNSUPPORTED (instantiating a graph allocates);
+ *  - step timing (ar_comm_set_step_timing) records nothing for this call.
+ * The call allocates nothing: no hipMalloc, hipFree, event or graph. The
+ * caller still owns the send and recv buffers and the stream.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: each step writes a slot
+ * before any later step reads it). Calls on one GPU that may overlap in time
+ * (unordered streams, several host threads) race on the array: the caller
+ * must order them. INVALID_ARGUMENT also if ar_comm_create could not look
+ * up the array's address on the comm's device (ar_last_error says why). */
+ar_result_t ar_all_reduce_noalloc(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
+                                  ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream);
 
 /* Reduce-scatter [P3 section 六; P4 section 五个原语]: sendbufs[r] holds
  * nranks*recvcount elements; recvbufs[c] (recvcount elements) receives

@@ -32,6 +32,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MAX_RANKS = 64  # AR_MAX_RANKS
 MAX_TENSORS = 65536  # AR_MAX_TENSORS
+NOALLOC_SCRATCH_BYTES = 64 << 20  # AR_NOALLOC_SCRATCH_BYTES
 
 # ar_result_t
 AR_SUCCESS, AR_ERR_INVALID_ARGUMENT, AR_ERR_UNSUPPORTED, AR_ERR_HIP, AR_ERR_OUT_OF_MEMORY, AR_ERR_INTERNAL = range(6)
@@ -51,7 +52,7 @@ MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph"
 
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",
-    "ar_all_reduce", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi",
+    "ar_all_reduce", "ar_all_reduce_noalloc", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi",
     "ar_comm_set_step_timing", "ar_comm_set_streaming", "ar_last_step_times_ms",
     "ar_result_string", "ar_last_error",
 )
@@ -67,6 +68,7 @@ _lib.ar_workspace_bytes.argtypes = [_c_int, _c_int, _c_size, _c_int, _c_int]
 _lib.ar_workspace_bytes.restype = _c_size
 _lib.ar_comm_set_workspace.argtypes = [_vp, _vp, _c_size]
 _lib.ar_all_reduce.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _c_int, _vp]
+_lib.ar_all_reduce_noalloc.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _c_int, _vp]
 _lib.ar_reduce_scatter.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _c_int, _vp]
 _lib.ar_all_gather.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _vp]
 _lib.ar_all_to_all.argtypes = [_vp, _ptr_array, _ptr_array, _c_size, _c_int, _c_int, _vp]
@@ -79,7 +81,8 @@ _lib.ar_result_string.argtypes = [_c_int]
 _lib.ar_result_string.restype = ctypes.c_char_p
 _lib.ar_last_error.argtypes = []
 _lib.ar_last_error.restype = ctypes.c_char_p
-for _name in ("ar_comm_create", "ar_comm_destroy", "ar_comm_set_workspace", "ar_all_reduce", "ar_reduce_scatter",
+for _name in ("ar_comm_create", "ar_comm_destroy", "ar_comm_set_workspace", "ar_all_reduce", "ar_all_reduce_noalloc",
+              "ar_reduce_scatter",
               "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi", "ar_comm_set_step_timing",
               "ar_comm_set_streaming", "ar_last_step_times_ms"):
     getattr(_lib, _name).restype = _c_int
@@ -224,6 +227,16 @@ def ar_all_reduce(comm, sendbufs, recvbufs, count: int, dtype, op, mode="fused",
     _check(_lib.ar_all_reduce(_h(comm), *_ptr_pair(sendbufs, recvbufs), count, _enum(dtype, DTYPE_NAMES, "dtype"),
                               _enum(op, OP_NAMES, "op"), _enum(mode, MODE_NAMES, "mode"),
                               _stream(stream, comm.device if isinstance(comm, Comm) else 0)), "ar_all_reduce")
+
+
+def ar_all_reduce_noalloc(comm, sendbufs, recvbufs, count: int, dtype, op, mode="fused", stream=None):
+    """ar_all_reduce with its partial sums in the library's device scratch
+    array instead of the comm's workspace; allocates nothing."""
+    _check(_lib.ar_all_reduce_noalloc(_h(comm), *_ptr_pair(sendbufs, recvbufs), count,
+                                      _enum(dtype, DTYPE_NAMES, "dtype"), _enum(op, OP_NAMES, "op"),
+                                      _enum(mode, MODE_NAMES, "mode"),
+                                      _stream(stream, comm.device if isinstance(comm, Comm) else 0)),
+           "ar_all_reduce_noalloc")
 
 
 def ar_reduce_scatter(comm, sendbufs, recvbufs, recvcount: int, dtype, op, mode="fused", stream=None):

@@ -27,7 +27,7 @@ OBJDIR = os.path.join(PKG, "_build")
 # compiled in parallel, then linked.
 SOURCES = [os.path.join(CSRC, f) for f in
            ("dtype_f32.hip", "dtype_f16.hip", "dtype_bf16.hip", "dtype_i32.hip", "tree_f32.hip", "tree_f16.hip",
-            "tree_bf16.hip", "tree_i32.hip", "kernels.hip", "api.cpp")]
+            "tree_bf16.hip", "tree_i32.hip", "kernels.hip", "noalloc.hip", "api.cpp")]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

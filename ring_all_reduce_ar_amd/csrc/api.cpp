@@ -41,6 +41,10 @@ struct ar_comm {
     std::vector<GraphEntry> graphs;
     uint64_t use_clock = 0;
     hipStream_t capture_stream = nullptr;
+    // ar_all_reduce_noalloc: this device's AR_NOALLOC_SCRATCH_BYTES array,
+    // looked up at creation (or why the lookup failed).
+    void* scratch = nullptr;
+    std::string scratch_err;
 };
 
 namespace {
@@ -284,13 +288,27 @@ ar_result_t check_common(ar_comm_t comm, const void* const* send, void* const* r
     return AR_SUCCESS;
 }
 
-ar_result_t need_workspace(const ar_comm* comm, size_t need)
+// The device memory a call keeps its partial sums in: the comm's attached
+// workspace, or the library's scratch array for ar_all_reduce_noalloc.
+struct Workspace {
+    void* ptr;
+    size_t bytes;
+    bool scratch;
+};
+
+Workspace comm_workspace(const ar_comm* comm) { return {comm->ws, comm->ws ? comm->ws_bytes : 0, false}; }
+
+ar_result_t need_workspace(const Workspace& ws, size_t need)
 {
     if (need == 0) return AR_SUCCESS;
-    if (!comm->ws || comm->ws_bytes < need)
+    if (ws.scratch && need > ws.bytes)
+        return fail(AR_ERR_INVALID_ARGUMENT,
+                    "this call needs %zu bytes of partial sums; the allocation-free call has %zu "
+                    "(AR_NOALLOC_SCRATCH_BYTES)", need, ws.bytes);
+    if (!ws.ptr || ws.bytes < need)
         return fail(AR_ERR_INVALID_ARGUMENT,
                     "this call needs a device workspace of %zu bytes (attached: %zu); see ar_workspace_bytes", need,
-                    comm->ws ? comm->ws_bytes : static_cast<size_t>(0));
+                    ws.bytes);
     return AR_SUCCESS;
 }
 
@@ -336,6 +354,18 @@ AR_EXPORT ar_result_t ar_comm_create(ar_comm_t* comm, int nranks, int hip_device
     c->num_cus = cus > 0 ? cus : 256;
     const char* dbg = std::getenv("AR_DEBUG");
     c->debug = dbg && *dbg && std::strcmp(dbg, "0") != 0;
+    {
+        // Set-up of ar_all_reduce_noalloc: this device's scratch array
+        // address, looked up with the device current. A failure only
+        // disables that entry point, which reports it.
+        DeviceGuard g(hip_device);
+        hipError_t se = g.err;
+        if (se == hipSuccess) se = ar::scratch_address(hip_device, &c->scratch);
+        if (se != hipSuccess) {
+            c->scratch = nullptr;
+            c->scratch_err = hipGetErrorString(se);
+        }
+    }
     *comm = c;
     return AR_SUCCESS;
 }
@@ -438,13 +468,19 @@ using Enqueue = std::function<hipError_t(hipStream_t, StepTimer*)>;
 
 hipError_t tick(StepTimer* t) { return t ? t->step() : hipSuccess; }
 
-// Eager: enqueue the launches directly on the caller's stream.
-ar_result_t run_eager(ar_comm* comm, hipStream_t stream, int nsteps, const Enqueue& fn)
+// Eager: enqueue the launches directly on the caller's stream. `timing`
+// false records no step events whatever the comm's setting (the
+// allocation-free call creates no events).
+ar_result_t run_eager(ar_comm* comm, hipStream_t stream, int nsteps, const Enqueue& fn, bool timing = true)
 {
+    if (!timing || !comm->step_timing) {
+        hipError_t e = fn(stream, nullptr);
+        return e != hipSuccess ? hip_fail(e, "kernel launch") : AR_SUCCESS;
+    }
     StepTimer timer(comm, stream);
     hipError_t e = timer.begin(nsteps);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = fn(stream, comm->step_timing ? &timer : nullptr);
+    e = fn(stream, &timer);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     timer.end();
     return AR_SUCCESS;
@@ -526,8 +562,9 @@ namespace {
 // The tree variant: a fused single pass in tree order, or 2*ceil(log2 n)
 // level launches (reduce up to rank 0, broadcast back down).
 ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
-                            ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
+                            ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream, const Workspace& wsp)
 {
+    const bool timing = !wsp.scratch;
     const int n = comm->nranks;
     const size_t e = elem_size(dtype);
     const uint64_t epv = 16 / e;
@@ -551,13 +588,13 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
-        });
+        }, timing);
     }
     int levels = 0;
     while ((1 << levels) < n) ++levels;
     ar::TreeArgs ta{};
     fill_ptrs(ta, n, sendbufs, recvbufs);
-    ta.ws = (dtype == AR_FLOAT16 || dtype == AR_BFLOAT16) ? comm->ws : nullptr;
+    ta.ws = (dtype == AR_FLOAT16 || dtype == AR_BFLOAT16) ? wsp.ptr : nullptr;
     ta.ws_stride = (count + 3) / 4 * 4;
     ta.count = count;
     ta.n = n;
@@ -579,16 +616,22 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         }
         return hipSuccess;
     };
-    return run_eager(comm, stream, 2 * levels, fn);
+    return run_eager(comm, stream, 2 * levels, fn, timing);
 }
 
 }  // namespace
 
-AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
-                                    ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
+namespace {
+
+// The all-reduce behind ar_all_reduce and ar_all_reduce_noalloc; `wsp` holds
+// the partial sums of the stepwise fp16/bf16 paths. The scratch array
+// (wsp.scratch) records no step events. Arguments are checked by the caller
+// for comm, arrays, dtype and mode.
+ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
+                            ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream, const Workspace& wsp)
 {
-    ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
-    if (rc != AR_SUCCESS) return rc;
+    ar_result_t rc = AR_SUCCESS;
+    const bool timing = !wsp.scratch;
     if (!valid_op(op)) return fail(AR_ERR_INVALID_ARGUMENT, "invalid op %d", static_cast<int>(op));
     const int n = comm->nranks;
     const size_t e = elem_size(dtype);
@@ -598,11 +641,12 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     const bool stepwise = ring_mode(mode) && n > 1;
     const size_t ws_need = ar_workspace_bytes(AR_COLL_ALL_REDUCE, n, count, dtype, mode);
     if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
-    rc = need_workspace(comm, ws_need);
+    rc = need_workspace(wsp, ws_need);
     if (rc != AR_SUCCESS) return rc;
-    rc = check_buffers(n, sendbufs, recvbufs, bytes, bytes, AR_COLL_ALL_REDUCE, e, comm->ws, ws_need);
+    rc = check_buffers(n, sendbufs, recvbufs, bytes, bytes, AR_COLL_ALL_REDUCE, e, wsp.ptr, ws_need);
     if (rc != AR_SUCCESS) return rc;
-    if (tree_mode(mode) && n > 1) return tree_all_reduce(comm, sendbufs, recvbufs, count, dtype, op, mode, stream);
+    if (tree_mode(mode) && n > 1)
+        return tree_all_reduce(comm, sendbufs, recvbufs, count, dtype, op, mode, stream, wsp);
 
     // Ring plan: q = ceil(count / n); chunk c = [c*q, min((c+1)*q, count)).
     const uint64_t q = ceil_div(count, static_cast<uint64_t>(n));
@@ -631,7 +675,7 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rank_major, gx, s);
             return err != hipSuccess ? err : tick(t);
-        });
+        }, timing);
     }
 
     // Reduce-scatter: n-1 steps. fp32/int32 partials travel in the recv
@@ -639,7 +683,7 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     // stay in fp32 in the workspace, one slot per element.
     ar::StepArgs sa{};
     fill_ptrs(sa, n, sendbufs, recvbufs);
-    sa.ws = (dtype == AR_FLOAT16 || dtype == AR_BFLOAT16) ? comm->ws : nullptr;
+    sa.ws = (dtype == AR_FLOAT16 || dtype == AR_BFLOAT16) ? wsp.ptr : nullptr;
     sa.count = count;
     sa.q = q;
     sa.n = n;
@@ -673,7 +717,33 @@ AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[]
     };
     if (mode == AR_MODE_RING_GRAPH)
         return run_graph(comm, graph_key(AR_COLL_ALL_REDUCE, n, sendbufs, recvbufs, count, dtype, op, sa.ws), stream, fn);
-    return run_eager(comm, stream, 2 * (n - 1), fn);
+    return run_eager(comm, stream, 2 * (n - 1), fn, timing);
+}
+
+}  // namespace
+
+AR_EXPORT ar_result_t ar_all_reduce(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[], size_t count,
+                                    ar_dtype_t dtype, ar_op_t op, ar_mode_t mode, hipStream_t stream)
+{
+    ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
+    if (rc != AR_SUCCESS) return rc;
+    return all_reduce_impl(comm, sendbufs, recvbufs, count, dtype, op, mode, stream, comm_workspace(comm));
+}
+
+AR_EXPORT ar_result_t ar_all_reduce_noalloc(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
+                                            size_t count, ar_dtype_t dtype, ar_op_t op, ar_mode_t mode,
+                                            hipStream_t stream)
+{
+    ar_result_t rc = check_common(comm, sendbufs, recvbufs, dtype, mode);
+    if (rc != AR_SUCCESS) return rc;
+    if (mode == AR_MODE_RING_GRAPH)
+        return fail(AR_ERR_UNSUPPORTED, "AR_MODE_RING_GRAPH instantiates a graph, which allocates; the "
+                                        "allocation-free call takes the other modes");
+    if (!comm->scratch)
+        return fail(AR_ERR_INVALID_ARGUMENT, "the scratch array's address on device %d is unknown: %s",
+                    comm->device, comm->scratch_err.c_str());
+    return all_reduce_impl(comm, sendbufs, recvbufs, count, dtype, op, mode, stream,
+                           Workspace{comm->scratch, AR_NOALLOC_SCRATCH_BYTES, true});
 }
 
 AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbufs[], void* const recvbufs[],
@@ -694,7 +764,7 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
     const bool stepwise = ring_mode(mode) && n > 1;
     const size_t ws_need = stepwise ? ar_workspace_bytes(AR_COLL_REDUCE_SCATTER, n, recvcount, dtype, mode) : 0;
     if (ws_need == static_cast<size_t>(-1)) return fail(AR_ERR_INVALID_ARGUMENT, "workspace size overflows");
-    rc = need_workspace(comm, ws_need);
+    rc = need_workspace(comm_workspace(comm), ws_need);
     if (rc != AR_SUCCESS) return rc;
     rc = check_buffers(n, sendbufs, recvbufs, sbytes, rbytes, AR_COLL_REDUCE_SCATTER, e, comm->ws, ws_need);
     if (rc != AR_SUCCESS) return rc;

@@ -169,4 +169,9 @@ hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t
 // send[r] -> recv[r] + r*dst_stride, total bytes, for every rank.
 hipError_t launch_local_copy(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);
 
+// The device address of this library's AR_NOALLOC_SCRATCH_BYTES scratch
+// array on `device`, which must be the current device; looked up once per
+// device and cached (noalloc.hip).
+hipError_t scratch_address(int device, void** out);
+
 }  // namespace ar
