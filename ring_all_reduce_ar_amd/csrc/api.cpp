@@ -211,16 +211,28 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
     return f;
 }
 
-// The rank-major all-reduce kernels (5..8 ranks, 16-byte vectors,
-// non-temporal access) for more than 128 MiB and at most 4 GiB per rank, at
-// 16 workgroups per CU; measured against the two-tile kernels on the same
-// buffers: +2.4 to +3.5 points at 256 MiB per rank, about +0.5 at 1-4 GiB.
-// (The reduce-scatter takes them at every size beyond the cache; see
-// ar_reduce_scatter.)
+// The rank-major all-reduce kernels (16-byte vectors, non-temporal access)
+// once the call's footprint exceeds the last-level cache: up to 4 GiB per
+// rank at 4..8 ranks, at every size above 8 ranks. Measured against the
+// kernels used before on the same buffers (fp32): at 8 ranks +10% at 64 and
+// 128 MiB per rank, +2.4 to +3.5 points at 256 MiB, about +0.5 at 1-4 GiB,
+// -1.1 to +0.6 at 14 GB (hence the 4 GiB bound); at 4 ranks +6.6% at
+// 256 MiB; above 8 ranks see fused_rank_major_any.
 bool use_rank_major(size_t bytes_per_rank, int nranks, bool vec, bool nt)
 {
-    return vec && nt && nranks >= 5 && nranks <= 8 && bytes_per_rank > (size_t(128) << 20) &&
-           bytes_per_rank <= (size_t(4) << 30);
+    if (!vec || !nt || nranks < 4) return false;
+    return nranks > 8 || bytes_per_rank <= (size_t(4) << 30);
+}
+
+// Workgroups per CU for the rank-major all-reduce: 16, and 32 above 32 ranks
+// (64 ranks x 256 MiB: 6.53 against 6.68 ms at 16).
+int rank_major_per_cu(int nranks) { return nranks > 32 ? 32 : 16; }
+
+// The multi-tensor call's rank-major tile (8 ranks, 128 MiB-4 GiB of bucket
+// per rank).
+bool use_rank_major_multi(size_t bytes_per_rank, int nranks, bool nt)
+{
+    return nt && nranks == 8 && bytes_per_rank > (size_t(128) << 20) && bytes_per_rank <= (size_t(4) << 30);
 }
 
 // Workgroups per CU for the fused all-reduce, from sweeps of 2..16 per CU in
@@ -670,8 +682,8 @@ ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* 
         const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
         const bool nt = nt_access(comm, beyond);
         const bool rank_major = use_rank_major(bytes, n, vec, beyond);
-        const int gx =
-            grid_for(comm, vec ? ceil_div(q, epv) : q, n, rank_major ? 16 : fused_per_cu(bytes, n, !beyond));
+        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n,
+                                rank_major ? rank_major_per_cu(n) : fused_per_cu(bytes, n, !beyond));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rank_major, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -789,12 +801,15 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.n = n;
         const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, sbytes, rbytes));
         const bool nt = nt_access(comm, beyond);
-        // Rank-major kernels at 5..8 ranks beyond the last-level cache: 16
-        // workgroups per CU up to 4 GiB of input per rank, 8 above (+9 points
-        // at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against the two-tile
-        // kernels on the same buffers).
-        const bool rank_major = vec && beyond && n >= 5 && n <= 8;
-        const int per_cu = rank_major ? (sbytes <= (size_t(4) << 30) ? 16 : 8) : (n <= 2 ? 4 : 8);
+        // Rank-major kernels beyond the last-level cache from 5 ranks up: at
+        // 5..8 ranks 16 workgroups per CU up to 4 GiB of input per rank, 8
+        // above (+9 points at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against
+        // the two-tile kernels on the same buffers); above 8 ranks the
+        // run-time rank-count body, as the all-reduce takes it.
+        const bool rank_major = vec && beyond && n >= 5;
+        const int per_cu = !rank_major ? (n <= 2 ? 4 : 8)
+                           : n > 8    ? rank_major_per_cu(n)
+                                      : (sbytes <= (size_t(4) << 30) ? 16 : 8);
         const int gx_f = grid_for(comm, vec ? ceil_div(q, epv) : q, n, per_cu);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, rank_major, gx_f, s);
@@ -1075,7 +1090,7 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
     // The rank-major kernel at 8 ranks, on the flat call's size rule (the
     // bucket's bytes per rank); its vector tiles are four kBlock-vector
     // quarters wide.
-    const bool rank_major = n == 8 && use_rank_major(total * e, n, true, beyond);
+    const bool rank_major = use_rank_major_multi(total * e, n, beyond);
     const uint64_t tile_vecs = rank_major ? ar::kMultiRankMajorTile : ar::kMultiVecTile;
 
     // Lays out tensors [t0, t1) of the plan as one table (pointer blocks,

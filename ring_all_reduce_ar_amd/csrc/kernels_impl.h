@@ -390,10 +390,14 @@ constexpr int kRankMajorTiles = 4;
 // Rank-major body of the fused reduction (NR ranks known at compile time): a
 // thread takes M consecutive tiles per grid-stride step and folds them one
 // rank at a time in ring order, so each stage reads M vectors from one rank
-// buffer (a workgroup streams M * 4 KiB contiguous from it), with the next
-// rank's loads issued before the current rank's combine (two stages in
-// flight). Then the M results go to every rank (all-reduce) or to the
-// chunk's output block (SCATTER). Each element's fold is the ring order of
+// buffer (a workgroup streams M * 4 KiB contiguous from it). The next rank's
+// loads are issued before the current rank's combine, but the copy of the
+// next rank's registers into the current ones makes each stage wait for its
+// loads, so a wave has one stage (M loads) in flight at a time; the other
+// waves of the CU (96 VGPRs: five per SIMD) cover the latency. A variant
+// with a real prefetch distance of 1-3 stages held 120-130 VGPRs and ran
+// 2-6% slower at 8 ranks x 64 MiB-1 GiB. Then the M results go to every rank
+// (all-reduce) or to the chunk's output block (SCATTER). Each element's fold is the ring order of
 // the two-tile body. Measured against the two-tile body on the same buffers
 // at 5-8 ranks: all-reduce +2.4 to +3.5 points at 256 MiB per rank, about
 // +0.5 at 1-4 GiB, -1.1 to +0.6 at 14 GB (so it stops at 4 GiB);
@@ -473,9 +477,130 @@ __device__ __forceinline__ void fused_rank_major(const ReduceArgs& a, int c, uin
     }
 }
 
-// RM selects the rank-major body (its own kernel, so its registers do not
-// lower the occupancy of the two-tile one).
-template <class F, int OP, int NR, bool SCATTER, bool NT, bool RM = false>
+// The M vectors of one rank folded into the accumulators (ring order:
+// incoming (+) the partial so far, as the two-tile body does).
+template <class F, int OP, int M>
+__device__ __forceinline__ void fold_stage(const u32x4 (&x)[M], typename F::Acc (&acc)[M][F::kEpv])
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        Acc t[E];
+        F::unpack(x[m], t);
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[m][j] = combine<OP>(t[j], acc[m][j]);
+    }
+}
+
+template <int M, bool NT>
+__device__ __forceinline__ void load_stage(u32x4 (&x)[M], const void* p, const uint64_t (&off)[M])
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m) x[m] = ldv_at<NT>(p, off[m]);
+}
+
+// Rank-major body for a rank count known only at run time: the super tile
+// (M consecutive tiles) is folded one rank at a time in ring order, as in
+// fused_rank_major, with two register sets that alternate between ranks, so
+// one rank's M loads stay in flight while the previous rank is combined
+// (the combine waits only for its own, older loads). The loads are
+// unconditional: lanes past the chunk read its first vector and drop it,
+// which keeps control flow out of the load-combine sequence (a guarded load
+// there makes every combine wait for all loads). The next rank's pointer is
+// fetched one stage ahead. Scheduling barriers pin the order. Measured
+// against the batched fold (fold_pair_any) on the same buffers, fp32:
+// +4 to +6% at 64 ranks x 256 MiB, +0.5 to +6% at 9-48 ranks x 256 MiB,
+// +9% at 16 ranks x 64 MiB; at 4 ranks x 256 MiB +6.6% over the two-tile
+// body.
+template <class F, int OP, bool NT, int M, bool SCATTER>
+__device__ __forceinline__ void fused_rank_major_any(const ReduceArgs& a, int c, uint64_t org, uint64_t v0,
+                                                     uint64_t v1, uint64_t ntiles, uint64_t rot)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    const int n = a.n;
+    const uint64_t G = gridDim.x;
+    const uint64_t nsup = (ntiles + M - 1) / M;
+    const uint64_t srot = nsup ? (rot / M) % nsup : 0;
+    for (uint64_t st = blockIdx.x; st < nsup; st += G) {
+        const uint64_t sr = st + srot < nsup ? st + srot : st + srot - nsup;
+        uint64_t vv[M], off[M];
+        bool ok[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint64_t tile = sr * M + m;
+            vv[m] = org + tile * kBlock + threadIdx.x;
+            ok[m] = tile < ntiles && vv[m] >= v0 && vv[m] < v1;
+            off[m] = (ok[m] ? vv[m] : v0) * 16;
+        }
+        Acc acc[M][E];
+        u32x4 xa[M], xb[M];
+        int r = c;
+        const void* p = a.send[r];
+        load_stage<M, NT>(xa, p, off);
+        r = r + 1 == n ? 0 : r + 1;
+        p = a.send[r];
+        if (n > 1) {
+            load_stage<M, NT>(xb, p, off);
+            r = r + 1 == n ? 0 : r + 1;
+            p = a.send[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < M; ++m) F::unpack(xa[m], acc[m]);
+        __builtin_amdgcn_sched_barrier(0);
+        int k = 1;  // xb holds fold position k (rank c + k)
+        for (; k + 2 < n; k += 2) {
+            load_stage<M, NT>(xa, p, off);
+            r = r + 1 == n ? 0 : r + 1;
+            p = a.send[r];
+            __builtin_amdgcn_sched_barrier(0);
+            fold_stage<F, OP, M>(xb, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            load_stage<M, NT>(xb, p, off);
+            r = r + 1 == n ? 0 : r + 1;
+            p = a.send[r];
+            __builtin_amdgcn_sched_barrier(0);
+            fold_stage<F, OP, M>(xa, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (k < n) {
+            if (k + 1 < n) {
+                load_stage<M, NT>(xa, p, off);
+                __builtin_amdgcn_sched_barrier(0);
+                fold_stage<F, OP, M>(xb, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                fold_stage<F, OP, M>(xa, acc);
+            } else {
+                fold_stage<F, OP, M>(xb, acc);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], n);
+            xa[m] = F::pack(acc[m]);
+        }
+        if constexpr (SCATTER) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (ok[m]) stv<NT>(a.recv[c], vv[m] - v0, xa[m]);
+        } else {
+            // rank by rank: M * 4 KiB back to back into each output buffer
+            for (int rr = 0; rr < n; ++rr)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (ok[m]) stv_at<NT>(a.recv[rr], off[m], xa[m]);
+        }
+    }
+}
+
+// RM > 0 selects a rank-major body with RM tiles per super tile: for NR
+// ranks known at compile time (fused_rank_major) or, with NR = 0, at run
+// time (fused_rank_major_any). Each is its own kernel, so its registers do
+// not lower the occupancy of the two-tile one.
+template <class F, int OP, int NR, bool SCATTER, bool NT, int RM = 0>
 __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
 {
     using Acc = typename F::Acc;
@@ -505,9 +630,10 @@ __global__ __launch_bounds__(kBlock) void fused_reduce_vec(const ReduceArgs a)
     const uint64_t org = SCATTER ? v0 : v0 / kBlock * kBlock;
     const uint64_t ntiles = nv ? (v1 - 1 - org) / kBlock + 1 : 0;
     const uint64_t rot = ntiles ? (static_cast<uint64_t>(c) * kRowSkewTiles) % ntiles : 0;
-    if constexpr (RM) {
-        static_assert(NR > 0, "the rank-major body is for fixed rank counts");
-        fused_rank_major<F, OP, NR, NT, kRankMajorTiles, SCATTER>(a, c, org, v0, v1, ntiles, rot);
+    if constexpr (RM > 0 && NR > 0) {
+        fused_rank_major<F, OP, NR, NT, RM, SCATTER>(a, c, org, v0, v1, ntiles, rot);
+    } else if constexpr (RM > 0) {
+        fused_rank_major_any<F, OP, NT, RM, SCATTER>(a, c, org, v0, v1, ntiles, rot);
     } else if constexpr (NR > 0) {
         fused_x2<F, OP, NR, SCATTER, NT>(a, c, org, v0, v1, ntiles, rot);
     } else {
@@ -1301,18 +1427,38 @@ hipError_t fused_nr(const ReduceArgs& a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
-// The rank-major kernels: 16-byte vectors, non-temporal access, 5..8 ranks
-// (the host picks them only there), either layout.
+// Tiles per super tile of the run-time rank-count rank-major kernel: 64 KiB
+// of fp32 per stage above 8 ranks and 16 KiB up to 8 (measured best of 2, 4,
+// 8 and 16 at 4-64 ranks); halved for 16-bit types, whose eight fp32
+// accumulators per vector would otherwise push the kernel past 128 VGPRs.
+template <class F>
+constexpr int rank_major_any_tiles(bool many)
+{
+    return (many ? 8 : 4) / (F::kEpv == 8 ? 2 : 1);
+}
+
+// The rank-major kernels: 16-byte vectors, non-temporal access, either
+// layout. 5..8 ranks take the fixed-rank-count body, other counts the
+// run-time one.
 template <class F, int OP, bool SC>
 hipError_t fused_nr_rank_major(const ReduceArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 block(kBlock);
+    constexpr int M = kRankMajorTiles;
     switch (a.n) {
-    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, true>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, true>), grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, true>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, true>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, M>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, M>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, M>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, M>), grid, block, 0, s, a); break;
+    default:
+        if (a.n > 8) {
+            constexpr int MA = rank_major_any_tiles<F>(true);
+            hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MA>), grid, block, 0, s, a);
+        } else {
+            constexpr int MA = rank_major_any_tiles<F>(false);
+            hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MA>), grid, block, 0, s, a);
+        }
+        break;
     }
     return hipGetLastError();
 }

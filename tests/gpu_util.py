@@ -97,8 +97,18 @@ def run_all_reduce(comm, xs, dtype, op, mode, inplace=False, offset=0, ws=None, 
     return [host(b.view) for b in recv], send, recv
 
 
+def oracle_threads() -> int:
+    """Host threads for the oracle's threaded fold (bit-identical to its
+    serial fold: tests/test_oracle_threads.py): the host's share for this
+    job (OMP_NUM_THREADS), else the affinity mask, at most 16."""
+    import os
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    t = int(env) if env.isdigit() and int(env) > 0 else len(os.sched_getaffinity(0))
+    return max(1, min(t, 16))
+
+
 def oracle_all_reduce(xs, dtype, op):
-    return oracle.fold_all_reduce([host(x) for x in xs], dtype, op)
+    return oracle.fold_all_reduce_threads([host(x) for x in xs], dtype, op, oracle_threads())
 
 
 def attach_workspace(comm, coll, n, count, dtype, mode):

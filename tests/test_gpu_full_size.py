@@ -248,13 +248,10 @@ def _generic_case(n, dtype, extra):
 @pytest.mark.parametrize("n,dtype,op,extra", [(17, "f32", "sum", 1), (33, "bf16", "avg", 3), (64, "f32", "prod", 1),
                                               (64, "f16", "max", 5), (12, "i32", "sum", 0)])
 def test_generic_rank_counts_full_compare(n, dtype, op, extra):
-    """Rank counts above 8 take the kernel whose rank count is a run-time
-    value; it folds two tiles per grid-stride iteration. These sizes give
-    every chunk row one iteration in which each workgroup holds two tiles and
-    a second in which only some hold a first tile and none a second, with
-    ragged chunks:
-    every element of every rank against the oracle, out of place, with guard
-    bands."""
+    """Rank counts above 8 take kernels whose rank count is a run-time value
+    (beyond the last-level cache, as here, the rank-major one), with ragged
+    chunks: every element of every rank against the oracle, out of place,
+    with guard bands."""
     count = _generic_case(n, dtype, extra)
     with ar.Comm(n, 0) as comm:
         xs = gu.make_inputs(n, count, dtype, op, seed=n)
@@ -288,6 +285,58 @@ def test_rank_major_range_full_compare(n, dtype, op, count, inplace):
     free()
 
 
+def _rank_major_any_case(n, dtype, extra):
+    # chunk rows of G + G/3 super tiles plus one tile, G being the row's
+    # workgroups (16 per CU, 32 above 32 ranks) and a super tile M tiles of
+    # 4 KiB (8 above 8 ranks, 4 up to 8, halved for 16-bit types): a full
+    # grid-stride pass, a second for a third of the workgroups, a last super
+    # tile holding one tile; `extra` elements make chunks start inside a vector
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = max(1, cus * (32 if n > 32 else 16) // n)
+    m = (8 if n > 8 else 4) // (2 if gu.ESIZE[dtype] == 2 else 1)
+    tiles = (g + g // 3) * m + 1
+    q = tiles * 256 * gu.EPV[dtype] + extra
+    return n * q - extra // 2
+
+
+@pytest.mark.parametrize("n,dtype,op,extra,inplace", [
+    (4, "f32", "sum", 1, True),
+    (4, "bf16", "avg", 3, False),
+    (16, "f32", "min", 2, False),
+    (12, "i32", "prod", 0, True),
+    (24, "f16", "sum", 5, False),
+])
+def test_rank_major_any_full_compare(n, dtype, op, extra, inplace):
+    """The rank-major kernel for run-time rank counts (4 ranks and above 8,
+    beyond the last-level cache): several grid-stride passes per chunk row,
+    a partial last super tile, ragged chunks; every element of every rank
+    against the oracle, with guard bands."""
+    count = _rank_major_any_case(n, dtype, extra)
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=n + extra)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "fused", inplace=inplace)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} inplace={inplace} rank {r}")
+        del xs, exp, got, send, recv
+    free()
+
+
+@pytest.mark.parametrize("n,dtype,op,count", [(8, "f32", "sum", 16_777_219), (6, "bf16", "max", 33_554_441)])
+def test_rank_major_from_64mib_full_compare(n, dtype, op, count):
+    """From 64 MiB per rank at 5-8 ranks (beyond the last-level cache) the
+    all-reduce takes the fixed-rank-count rank-major kernel: every element
+    of every rank, in place as the benchmark calls it, ragged chunks."""
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=count % 997)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "fused", inplace=True)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} rank {r}")
+        del xs, exp, got, send, recv
+    free()
+
+
 @pytest.mark.parametrize("n,count,dtype", [(8, 1 << 30, "f32"), (8, (1 << 31) - 5, "f16"), (6, 999_999_997, "f32")])
 def test_rank_major_upper_sizes_sampled(n, count, dtype):
     """At and below the rank-major kernels' 4 GiB-per-rank bound, in place as
@@ -305,13 +354,17 @@ def test_rank_major_upper_sizes_sampled(n, count, dtype):
     (5, "f16", "avg", 14_000_008, True),
     (7, "bf16", "max", 9_999_992, False),
     (6, "i32", "sum", 6_000_004, True),
+    (16, "f32", "sum", 1_000_004, False),
+    (64, "bf16", "avg", 70_000, True),
+    (12, "i32", "max", 3_000_000, False),
 ])
 def test_reduce_scatter_rank_major_full_compare(n, dtype, op, rc, inplace):
-    """Reduce-scatter at 5-8 ranks beyond the last-level cache takes the
-    rank-major kernels (block lengths here are whole 16-byte vectors, as the
-    vector kernels need): every element of every rank's block against the
-    oracle's reduce-scatter, out of place or in place (recv[r] inside send[r]
-    at block r), with guard bands."""
+    """Reduce-scatter from 5 ranks beyond the last-level cache takes the
+    rank-major kernels (fixed rank count up to 8, run-time above; block
+    lengths here are whole 16-byte vectors, as the vector kernels need):
+    every element of every rank's block against the oracle's reduce-scatter,
+    out of place or in place (recv[r] inside send[r] at block r), with guard
+    bands."""
     xs = gu.make_inputs(n, n * rc, dtype, op, seed=rc % 1000)
     exp = oracle.reduce_scatter([gu.host(x) for x in xs], dtype, op)
     with ar.Comm(n, 0) as comm:
