@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grad7b]
                     [--mode fused|stepwise|graph|tree|tree_stepwise]
                     [--collective all_reduce|reduce_scatter|all_gather|all_to_all]
-                    [--multi] [--streaming] [--no-cpu-baseline]
+                    [--multi] [--access auto|streaming|cached] [--no-cpu-baseline]
     python bench.py --sweep            # 1 KiB..256 MiB per rank, every mode, alpha-beta fit
     python bench.py --copy-probe BYTES # a plain device copy (HBM counter calibration)
 
@@ -428,9 +428,11 @@ def main():
                          "count in and out (out of place)")
     ap.add_argument("--multi", action="store_true",
                     help="bucket64/bucket8: reduce the bucket as its mixed-size tensors with ar_all_reduce_multi")
-    ap.add_argument("--streaming", action="store_true",
-                    help="non-temporal loads and stores at every size in the one-launch calls "
-                         "(ar_comm_set_streaming); by default only beyond the 256 MB last-level cache")
+    ap.add_argument("--access", default="auto", choices=["auto", "streaming", "cached"],
+                    help="access flavour of the one-launch calls (ar_comm_set_access): auto streams the all-reduce "
+                         "above half the 256 MB last-level cache and the other collectives above all of it; "
+                         "streaming always; cached whenever the footprint fits the cache")
+    ap.add_argument("--streaming", action="store_true", help="the same as --access streaming")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line, sweep 1 KiB .. 256 MiB per rank (8 ranks, fp32 SUM) in every "
@@ -467,7 +469,8 @@ def main():
     wl = wl if wl in synthetic.WORKLOAD_IDS else "sweep"
     comm = ar.Comm(n, 0)
     if args.streaming:
-        ar.ar_comm_set_streaming(comm, True)
+        args.access = "streaming"
+    ar.ar_comm_set_access(comm, args.access)
     stream = torch.cuda.current_stream()
     sizes = None
     coll = args.collective
@@ -483,8 +486,8 @@ def main():
             sys.exit(2)
         sizes = synthetic.bucket_sizes(count, ESIZE[dtype], 4096, 64 << 20, seed=5)
         desc += f"; as {len(sizes)} tensors per rank through ar_all_reduce_multi"
-    if args.streaming:
-        desc += "; streaming (non-temporal) access"
+    if args.access != "auto":
+        desc += f"; {args.access} access (ar_comm_set_access)"
 
     s_bytes = count * ESIZE[dtype]
     # A call whose rank buffers fit in the last-level cache would be timed
@@ -583,7 +586,7 @@ def main():
     alg_bytes = (2 * n if coll in ("all_reduce", "all_to_all") else n + 1) * s_bytes
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     # counter summaries cover the default access rule and the flat call
-    traffic = None if args.multi or args.streaming else load_traffic(args.workload, args.mode, coll)
+    traffic = None if args.multi or args.access != "auto" else load_traffic(args.workload, args.mode, coll)
     result = {
         "metric": METRIC,
         "value": sig(algbw),
@@ -603,7 +606,8 @@ def main():
         "config": {"workload": desc, "nranks": n, "count_per_rank": count, "bytes_per_rank": s_bytes, "op": op,
                    "mode": args.mode, "collective": coll,
                    "accumulate": "f32" if dtype in ("f16", "bf16") else dtype,
-                   "access": "streaming" if args.streaming else "non-temporal beyond the last-level cache",
+                   "access": args.access if args.access != "auto" else
+                   "auto: non-temporal above half the last-level cache (all-reduce) or all of it (others)",
                    "parallelism": f"{n} virtual ranks on 1 GPU"},
         "busbw": sig(busbw),
         "hbm_gbps": sig(achieved),
@@ -644,7 +648,7 @@ def main():
             "note": "step_us: events between the launches of one call (median over K calls); alpha_device_us "
                     "their mean; alpha_call_us: ms_per_step over the launches (host enqueue included)"}
     if (args.workload == "grad7b" and coll == "all_reduce" and args.mode == "fused" and not args.multi
-            and not args.streaming and not args.no_range):
+            and args.access == "auto" and not args.no_range):
         # the metric's range below the headline: 8 ranks x 64 MiB, 256 MiB and
         # the cold 25 MiB DDP bucket, against the same copy ceiling
         result["range"] = []

@@ -117,6 +117,13 @@ typedef enum {
     AR_MODE_TREE_STEPWISE = 4
 } ar_mode_t;
 
+/* Access flavour of the one-launch calls; see ar_comm_set_access. */
+typedef enum {
+    AR_ACCESS_AUTO = 0,
+    AR_ACCESS_STREAMING = 1,
+    AR_ACCESS_CACHED = 2
+} ar_access_t;
+
 typedef enum {
     AR_COLL_ALL_REDUCE = 0,
     AR_COLL_REDUCE_SCATTER = 1,
@@ -257,17 +264,29 @@ ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const void* const 
  * per-step overhead and is not meant for the caller's own graph capture. */
 ar_result_t ar_comm_set_step_timing(ar_comm_t comm, int enable);
 
-/* Streaming access, off by default. The one-launch calls (fused and tree
- * all-reduce, fused reduce-scatter, all-gather and all-to-all, multi-tensor
- * all-reduce) use non-temporal loads and stores when the call's distinct
- * bytes exceed the 256 MB last-level cache, and cached ones below it, which
- * suits buffers a kernel has just written (a gradient bucket after the
- * backward pass). With enable != 0 they use non-temporal access at every
- * size: for buffers that come from HBM, e.g. 8 ranks x 16-32 MiB fp32 ran
- * 4-9% faster that way when not in the cache, and 5-28% slower when still in
- * it. Launch shapes and results (bit for bit) are the same either way; the
- * ring-stepwise and graph modes keep the size rule. The setting is per comm
- * and takes effect from the next call. NULL comm: INVALID_ARGUMENT. */
+/* Access flavour of the one-launch calls (fused and tree all-reduce, fused
+ * reduce-scatter, all-gather and all-to-all, multi-tensor all-reduce): with
+ * non-temporal ("streaming") loads and stores, which pass data through the
+ * caches without keeping it, or with ordinary cached ones, which let a call
+ * on buffers still in the 256 MB last-level cache run from it.
+ *  AR_ACCESS_AUTO (the default): non-temporal when the call's distinct bytes
+ *    exceed half the last-level cache for the all-reduce (a footprint that
+ *    large is unlikely to be resident in full, and cold calls gain more than
+ *    warm ones lose: 8 ranks x 25 MiB fp32, 73 against 86 us cold, 71
+ *    against 62 us warm) and the whole cache for the other collectives;
+ *  AR_ACCESS_STREAMING: non-temporal at every size, for buffers known to
+ *    come from HBM;
+ *  AR_ACCESS_CACHED: cached whenever the footprint fits in the cache, for
+ *    buffers a kernel has just written (e.g. a gradient bucket right after
+ *    the backward pass).
+ * Launch shapes follow the flavour chosen; results are the same bits either
+ * way. The ring-stepwise and graph modes always use cached access except the
+ * all-to-all steps beyond the cache. The setting is per comm and takes
+ * effect from the next call. NULL comm or an unknown value:
+ * INVALID_ARGUMENT. */
+ar_result_t ar_comm_set_access(ar_comm_t comm, ar_access_t access);
+
+/* ar_comm_set_access(comm, enable ? AR_ACCESS_STREAMING : AR_ACCESS_AUTO). */
 ar_result_t ar_comm_set_streaming(ar_comm_t comm, int enable);
 
 /* Step durations (ms) of the last timed call on this comm: waits for that

@@ -42,6 +42,9 @@ AR_FLOAT32, AR_FLOAT16, AR_BFLOAT16, AR_INT32 = range(4)
 AR_SUM, AR_AVG, AR_MAX, AR_MIN, AR_PROD = range(5)
 # ar_mode_t
 AR_MODE_FUSED, AR_MODE_RING_STEPWISE, AR_MODE_RING_GRAPH, AR_MODE_TREE, AR_MODE_TREE_STEPWISE = range(5)
+# ar_access_t
+AR_ACCESS_AUTO, AR_ACCESS_STREAMING, AR_ACCESS_CACHED = range(3)
+ACCESS_NAMES = {"auto": AR_ACCESS_AUTO, "streaming": AR_ACCESS_STREAMING, "cached": AR_ACCESS_CACHED}
 # ar_collective_t
 AR_COLL_ALL_REDUCE, AR_COLL_REDUCE_SCATTER, AR_COLL_ALL_GATHER, AR_COLL_ALL_TO_ALL = range(4)
 
@@ -53,7 +56,7 @@ MODE_NAMES = {"fused": AR_MODE_FUSED, "stepwise": AR_MODE_RING_STEPWISE, "graph"
 EXPORTED_SYMBOLS = (
     "ar_comm_create", "ar_comm_destroy", "ar_comm_nranks", "ar_workspace_bytes", "ar_comm_set_workspace",
     "ar_all_reduce", "ar_all_reduce_noalloc", "ar_reduce_scatter", "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi",
-    "ar_comm_set_step_timing", "ar_comm_set_streaming", "ar_last_step_times_ms",
+    "ar_comm_set_step_timing", "ar_comm_set_access", "ar_comm_set_streaming", "ar_last_step_times_ms",
     "ar_result_string", "ar_last_error",
 )
 
@@ -76,6 +79,7 @@ _lib.ar_all_reduce_multi.argtypes = [_vp, _c_int, _ptr_array, _ptr_array, ctypes
                                      _c_int, _vp]
 _lib.ar_comm_set_step_timing.argtypes = [_vp, _c_int]
 _lib.ar_comm_set_streaming.argtypes = [_vp, _c_int]
+_lib.ar_comm_set_access.argtypes = [_vp, _c_int]
 _lib.ar_last_step_times_ms.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)]
 _lib.ar_result_string.argtypes = [_c_int]
 _lib.ar_result_string.restype = ctypes.c_char_p
@@ -84,7 +88,7 @@ _lib.ar_last_error.restype = ctypes.c_char_p
 for _name in ("ar_comm_create", "ar_comm_destroy", "ar_comm_set_workspace", "ar_all_reduce", "ar_all_reduce_noalloc",
               "ar_reduce_scatter",
               "ar_all_gather", "ar_all_to_all", "ar_all_reduce_multi", "ar_comm_set_step_timing",
-              "ar_comm_set_streaming", "ar_last_step_times_ms"):
+              "ar_comm_set_streaming", "ar_comm_set_access", "ar_last_step_times_ms"):
     getattr(_lib, _name).restype = _c_int
 
 
@@ -277,6 +281,11 @@ def ar_comm_set_step_timing(comm, enable: bool):
 
 def ar_comm_set_streaming(comm, enable: bool):
     _check(_lib.ar_comm_set_streaming(_h(comm), 1 if enable else 0), "ar_comm_set_streaming")
+
+
+def ar_comm_set_access(comm, access):
+    """access: "auto", "streaming", "cached" or an AR_ACCESS_* value."""
+    _check(_lib.ar_comm_set_access(_h(comm), _enum(access, ACCESS_NAMES, "access")), "ar_comm_set_access")
 
 
 def ar_last_step_times_ms(comm, cap: int = 2 * MAX_RANKS + 1):

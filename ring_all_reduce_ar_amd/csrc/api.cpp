@@ -28,7 +28,7 @@ struct ar_comm {
     size_t ws_bytes = 0;
     bool debug = false;
     bool step_timing = false;
-    bool streaming = false;  // non-temporal access in the one-launch calls whatever the footprint
+    ar_access_t access = AR_ACCESS_AUTO;  // access flavour of the one-launch calls (ar_comm_set_access)
     std::vector<hipEvent_t> events;  // step boundaries of the last timed call
     int last_steps = -1;
     // AR_MODE_RING_GRAPH: instantiated graphs keyed by call signature.
@@ -195,9 +195,30 @@ constexpr uint64_t kLastLevelCacheBytes = uint64_t(256) << 20;
 
 bool use_nt(uint64_t footprint_bytes) { return footprint_bytes > kLastLevelCacheBytes; }
 
-// The access flavour of a one-launch call: non-temporal beyond the cache, or
-// always when the comm is set to streaming. Launch shapes follow `beyond`.
-bool nt_access(const ar_comm* comm, bool beyond) { return beyond || comm->streaming; }
+// Above this footprint the fused all-reduce streams by default. A footprint
+// of more than half the cache is unlikely to be resident in full, and cold
+// calls gain more from non-temporal access than warm ones lose: 8 ranks,
+// fp32, cold (every call from HBM) / warm (repeated on one buffer set), in
+// microseconds, cached two-tile against non-temporal rank-major kernels:
+// 16 MiB per rank 57.8 / 41.4 against 53.0 / 50.1 (below the threshold);
+// 20 MiB 71.5 / 50.4 against 61.0 / 58.6; 25 MiB 86.3 / 61.5 against
+// 73.2 / 70.6; 32 MiB 108.6 / 78.1 against 87.4 / 85.6. Streaming wins
+// unless the data is warm more than 55-75% of the time.
+constexpr uint64_t kAllReduceStreamBytes = kLastLevelCacheBytes / 2;
+
+// The access flavour of a one-launch call (ar_comm_set_access): AUTO streams
+// (non-temporal loads and stores) above `auto_bytes` of footprint
+// (kAllReduceStreamBytes for the all-reduce, the whole cache for the other
+// collectives), STREAMING always, CACHED above the whole cache only. The
+// launch shapes follow the flavour chosen.
+bool call_nt(const ar_comm* comm, uint64_t footprint_bytes, uint64_t auto_bytes)
+{
+    switch (comm->access) {
+    case AR_ACCESS_STREAMING: return true;
+    case AR_ACCESS_CACHED: return footprint_bytes > kLastLevelCacheBytes;
+    default: return footprint_bytes > auto_bytes;
+    }
+}
 
 // Distinct bytes of the rank buffers: in-place ranks count once.
 uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t send_bytes, uint64_t recv_bytes)
@@ -212,27 +233,34 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
 }
 
 // The rank-major all-reduce kernels (16-byte vectors, non-temporal access)
-// once the call's footprint exceeds the last-level cache: up to 4 GiB per
-// rank at 4..8 ranks, at every size above 8 ranks. Measured against the
-// kernels used before on the same buffers (fp32): at 8 ranks +10% at 64 and
-// 128 MiB per rank, +2.4 to +3.5 points at 256 MiB, about +0.5 at 1-4 GiB,
-// -1.1 to +0.6 at 14 GB (hence the 4 GiB bound); at 4 ranks +6.6% at
-// 256 MiB; above 8 ranks see fused_rank_major_any.
+// whenever the call streams: up to 4 GiB per rank at 4..8 ranks, at every
+// size above 8 ranks. Measured against the kernels used before on the same
+// buffers (fp32): at 8 ranks +15% cold at 20-32 MiB per rank, +10% at 64
+// and 128 MiB, +2.4 to +3.5 points at 256 MiB, about +0.5 at 1-4 GiB, -1.1
+// to +0.6 at 14 GB (hence the 4 GiB bound); at 4 ranks +16% cold at 40 MiB
+// and +6.6% at 256 MiB; above 8 ranks see fused_rank_major_any.
 bool use_rank_major(size_t bytes_per_rank, int nranks, bool vec, bool nt)
 {
     if (!vec || !nt || nranks < 4) return false;
     return nranks > 8 || bytes_per_rank <= (size_t(4) << 30);
 }
 
-// Workgroups per CU for the rank-major all-reduce: 16, and 32 above 32 ranks
-// (64 ranks x 256 MiB: 6.53 against 6.68 ms at 16).
-int rank_major_per_cu(int nranks) { return nranks > 32 ? 32 : 16; }
+// Workgroups per CU for the rank-major all-reduce: 32 from 32 ranks (64 ranks
+// x 256 MiB: 6.52 against 6.65 ms at 16; 32 ranks: 3.21 against 3.29 ms),
+// else 8 up to 32 MiB per rank (8 x 25 MiB cold: 73.2 against 76.6 us at 16)
+// and 16 above (8 x 64 MiB: 0.179 against 0.188 ms at 8).
+int rank_major_per_cu(int nranks, size_t bytes_per_rank)
+{
+    if (nranks >= 32) return 32;
+    return bytes_per_rank <= (size_t(32) << 20) ? 8 : 16;
+}
 
-// The multi-tensor call's rank-major tile (8 ranks, 128 MiB-4 GiB of bucket
-// per rank).
+// The multi-tensor call's rank-major tiles beyond the last-level cache: at 8
+// ranks for 128 MiB-4 GiB of bucket per rank, above 8 ranks at every size.
 bool use_rank_major_multi(size_t bytes_per_rank, int nranks, bool nt)
 {
-    return nt && nranks == 8 && bytes_per_rank > (size_t(128) << 20) && bytes_per_rank <= (size_t(4) << 30);
+    if (!nt || nranks < 8) return false;
+    return nranks > 8 || (bytes_per_rank > (size_t(128) << 20) && bytes_per_rank <= (size_t(4) << 30));
 }
 
 // Workgroups per CU for the fused all-reduce, from sweeps of 2..16 per CU in
@@ -441,11 +469,18 @@ AR_EXPORT ar_result_t ar_comm_set_step_timing(ar_comm_t comm, int enable)
     return AR_SUCCESS;
 }
 
-AR_EXPORT ar_result_t ar_comm_set_streaming(ar_comm_t comm, int enable)
+AR_EXPORT ar_result_t ar_comm_set_access(ar_comm_t comm, ar_access_t access)
 {
     if (!comm) return fail(AR_ERR_INVALID_ARGUMENT, "comm is NULL");
-    comm->streaming = enable != 0;
+    if (access < AR_ACCESS_AUTO || access > AR_ACCESS_CACHED)
+        return fail(AR_ERR_INVALID_ARGUMENT, "invalid access flavour %d", static_cast<int>(access));
+    comm->access = access;
     return AR_SUCCESS;
+}
+
+AR_EXPORT ar_result_t ar_comm_set_streaming(ar_comm_t comm, int enable)
+{
+    return ar_comm_set_access(comm, enable ? AR_ACCESS_STREAMING : AR_ACCESS_AUTO);
 }
 
 AR_EXPORT ar_result_t ar_last_step_times_ms(ar_comm_t comm, float* out, int cap, int* nsteps)
@@ -596,7 +631,7 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         // per rank or at 32+ ranks, 8 above (measured ±2-3% at 8 ranks)
         const int per_cu = (count * e <= (size_t(128) << 20) || n >= 32) ? 16 : 8;
         const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, per_cu);
-        const bool nt = nt_access(comm, use_nt(footprint(n, sendbufs, recvbufs, count * e, count * e)));
+        const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, count * e, count * e), kLastLevelCacheBytes);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -679,11 +714,10 @@ ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* 
         a.count = count;
         a.q = q;
         a.n = n;
-        const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, bytes, bytes));
-        const bool nt = nt_access(comm, beyond);
-        const bool rank_major = use_rank_major(bytes, n, vec, beyond);
+        const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, bytes, bytes), kAllReduceStreamBytes);
+        const bool rank_major = use_rank_major(bytes, n, vec, nt);
         const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n,
-                                rank_major ? rank_major_per_cu(n) : fused_per_cu(bytes, n, !beyond));
+                                rank_major ? rank_major_per_cu(n, bytes) : fused_per_cu(bytes, n, !nt));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rank_major, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -799,16 +833,15 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.count = total;
         a.q = q;
         a.n = n;
-        const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, sbytes, rbytes));
-        const bool nt = nt_access(comm, beyond);
+        const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, sbytes, rbytes), kLastLevelCacheBytes);
         // Rank-major kernels beyond the last-level cache from 5 ranks up: at
         // 5..8 ranks 16 workgroups per CU up to 4 GiB of input per rank, 8
         // above (+9 points at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against
         // the two-tile kernels on the same buffers); above 8 ranks the
         // run-time rank-count body, as the all-reduce takes it.
-        const bool rank_major = vec && beyond && n >= 5;
+        const bool rank_major = vec && nt && n >= 5;
         const int per_cu = !rank_major ? (n <= 2 ? 4 : 8)
-                           : n > 8    ? rank_major_per_cu(n)
+                           : n > 8    ? rank_major_per_cu(n, sbytes)
                                       : (sbytes <= (size_t(4) << 30) ? 16 : 8);
         const int gx_f = grid_for(comm, vec ? ceil_div(q, epv) : q, n, per_cu);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
@@ -874,13 +907,12 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
         fill_ptrs(a, n, sendbufs, recvbufs);
         a.total = blk;
         a.n = n;
-        const bool beyond = use_nt(footprint(n, sendbufs, recvbufs, blk, rbytes));
-        const bool nt = nt_access(comm, beyond);
+        const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, blk, rbytes), kLastLevelCacheBytes);
         // Rank-major copy at 5..8 ranks from 512 MiB of input per rank
         // (measured against the copy above at 8 ranks: +7.4 points at
         // 512 MiB, +1.0 at 1 GiB, +6.6 at 1.75 GB; 1-4 points slower at
         // 64-256 MiB).
-        const bool rank_major = vec && beyond && n >= 5 && n <= 8 && blk >= (size_t(512) << 20);
+        const bool rank_major = vec && nt && n >= 5 && n <= 8 && blk >= (size_t(512) << 20);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_gather(a, vec, nt, rank_major, gx_f, s);
             return err != hipSuccess ? err : tick(t);
@@ -959,7 +991,7 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
         // 4 workgroups per CU: each moves one block pair, a plain copy stream
         // (8 ranks x 256 MiB: 69.3% against 62.2% at 8)
         const int gx = grid_for(comm, units, n * n, 4);
-        const bool nt1 = nt_access(comm, nt);
+        const bool nt1 = call_nt(comm, 2 * static_cast<uint64_t>(n) * total, kLastLevelCacheBytes);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_all_to_all(a, vec, nt1, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -1085,13 +1117,15 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
 
     uint64_t touched = 0;
     for (const Interval& x : iv) touched += x.hi - x.lo;
-    const bool beyond = use_nt(touched);
-    const bool nt = nt_access(comm, beyond);
-    // The rank-major kernel at 8 ranks, on the flat call's size rule (the
-    // bucket's bytes per rank); its vector tiles are four kBlock-vector
-    // quarters wide.
-    const bool rank_major = use_rank_major_multi(total * e, n, beyond);
-    const uint64_t tile_vecs = rank_major ? ar::kMultiRankMajorTile : ar::kMultiVecTile;
+    const bool nt = call_nt(comm, touched, kAllReduceStreamBytes);
+    // The rank-major kernels (use_rank_major_multi: the bucket's bytes per
+    // rank); their vector tiles are four kBlock-vector quarters wide at 8
+    // ranks, rank_major_any_tiles quarters above.
+    const bool rank_major = use_rank_major_multi(total * e, n, nt);
+    const uint64_t tile_vecs = !rank_major ? ar::kMultiVecTile
+                               : n == 8   ? ar::kMultiRankMajorTile
+                                          : static_cast<uint64_t>(ar::rank_major_any_tiles(n, static_cast<int>(e))) *
+                                                ar::kBlock;
 
     // Lays out tensors [t0, t1) of the plan as one table (pointer blocks,
     // then pieces with their first tiles) and returns its header.
@@ -1137,7 +1171,8 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
     // 16 workgroups per CU: the 29-tensor 256 MiB bucket ran at 7.09 ms at 64
     // ranks (flat: 7.05) against 7.51 at 8 per CU, and 0.913 against 0.929 ms
     // at 8 ranks.
-    const int cap = comm->num_cus * 16;
+    // The rank-major tiles above 32 ranks take 32 per CU, as the flat call.
+    const int cap = comm->num_cus * (rank_major && n > 32 ? 32 : 16);
 
     // The tables go in the kernel arguments, one launch per batch of tensors
     // that fits. (A table in device memory, written once and read by a single

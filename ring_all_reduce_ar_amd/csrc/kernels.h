@@ -118,6 +118,18 @@ constexpr int kMultiBlobBytes = 3840;
 // pieces into tiles of kBlock elements.
 constexpr int kMultiVecTile = 2 * kBlock;
 constexpr int kMultiRankMajorTile = 4 * kBlock;
+
+// Tiles (of kBlock 16-byte vectors) per super tile of the rank-major kernels
+// for run-time rank counts: 8 above 8 ranks and 4 up to 8 for 4-byte types
+// (64 and 16 KiB per rank and stage; measured best of 2, 4, 8 and 16 at
+// 4-64 ranks), half that for 2-byte types, whose eight fp32 accumulators
+// per vector would otherwise push the kernel past 128 VGPRs. Shared by the
+// kernels and the multi-tensor planner, which cuts pieces into such tiles.
+constexpr int kRankMajorAnyMany = 9;  // a rank count above 8
+__host__ __device__ constexpr int rank_major_any_tiles(int nranks, int elem_bytes)
+{
+    return (nranks > 8 ? 8 : 4) / (elem_bytes == 2 ? 2 : 1);
+}
 struct MultiHeader {
     int n;
     int npieces;
@@ -131,8 +143,9 @@ struct MultiArgs {
     alignas(16) unsigned char blob[kMultiBlobBytes];
 };
 
-// `rank_major` selects the rank-major kernel (needs nt and 8 ranks; the
-// table's vector tiles are then kMultiRankMajorTile vectors wide).
+// `rank_major` selects the rank-major kernel (needs nt and at least 8 ranks;
+// the table's vector tiles are then kMultiRankMajorTile vectors wide at 8
+// ranks, rank_major_any_tiles(n, elem) * kBlock above).
 hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, bool rank_major, int grid_x,
                                hipStream_t stream);
 

@@ -513,6 +513,56 @@ __device__ __forceinline__ void load_stage(u32x4 (&x)[M], const void* p, const u
 // +4 to +6% at 64 ranks x 256 MiB, +0.5 to +6% at 9-48 ranks x 256 MiB,
 // +9% at 16 ranks x 64 MiB; at 4 ranks x 256 MiB +6.6% over the two-tile
 // body.
+// The fold of fused_rank_major_any: M vectors per rank at byte offsets off
+// (every one readable) from the n ranks send[c], send[c+1], ... (mod n),
+// into acc, ring order.
+template <class F, int OP, bool NT, int M>
+__device__ __forceinline__ void fold_rank_major_any(const void* const* send, int c, int n, const uint64_t (&off)[M],
+                                                    typename F::Acc (&acc)[M][F::kEpv])
+{
+    u32x4 xa[M], xb[M];
+    int r = c;
+    const void* p = send[r];
+    load_stage<M, NT>(xa, p, off);
+    r = r + 1 == n ? 0 : r + 1;
+    p = send[r];
+    if (n > 1) {
+        load_stage<M, NT>(xb, p, off);
+        r = r + 1 == n ? 0 : r + 1;
+        p = send[r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < M; ++m) F::unpack(xa[m], acc[m]);
+    __builtin_amdgcn_sched_barrier(0);
+    int k = 1;  // xb holds fold position k (rank c + k)
+    for (; k + 2 < n; k += 2) {
+        load_stage<M, NT>(xa, p, off);
+        r = r + 1 == n ? 0 : r + 1;
+        p = send[r];
+        __builtin_amdgcn_sched_barrier(0);
+        fold_stage<F, OP, M>(xb, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage<M, NT>(xb, p, off);
+        r = r + 1 == n ? 0 : r + 1;
+        p = send[r];
+        __builtin_amdgcn_sched_barrier(0);
+        fold_stage<F, OP, M>(xa, acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k < n) {
+        if (k + 1 < n) {
+            load_stage<M, NT>(xa, p, off);
+            __builtin_amdgcn_sched_barrier(0);
+            fold_stage<F, OP, M>(xb, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            fold_stage<F, OP, M>(xa, acc);
+        } else {
+            fold_stage<F, OP, M>(xb, acc);
+        }
+    }
+}
+
 template <class F, int OP, bool NT, int M, bool SCATTER>
 __device__ __forceinline__ void fused_rank_major_any(const ReduceArgs& a, int c, uint64_t org, uint64_t v0,
                                                      uint64_t v1, uint64_t ntiles, uint64_t rot)
@@ -535,47 +585,8 @@ __device__ __forceinline__ void fused_rank_major_any(const ReduceArgs& a, int c,
             off[m] = (ok[m] ? vv[m] : v0) * 16;
         }
         Acc acc[M][E];
-        u32x4 xa[M], xb[M];
-        int r = c;
-        const void* p = a.send[r];
-        load_stage<M, NT>(xa, p, off);
-        r = r + 1 == n ? 0 : r + 1;
-        p = a.send[r];
-        if (n > 1) {
-            load_stage<M, NT>(xb, p, off);
-            r = r + 1 == n ? 0 : r + 1;
-            p = a.send[r];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < M; ++m) F::unpack(xa[m], acc[m]);
-        __builtin_amdgcn_sched_barrier(0);
-        int k = 1;  // xb holds fold position k (rank c + k)
-        for (; k + 2 < n; k += 2) {
-            load_stage<M, NT>(xa, p, off);
-            r = r + 1 == n ? 0 : r + 1;
-            p = a.send[r];
-            __builtin_amdgcn_sched_barrier(0);
-            fold_stage<F, OP, M>(xb, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            load_stage<M, NT>(xb, p, off);
-            r = r + 1 == n ? 0 : r + 1;
-            p = a.send[r];
-            __builtin_amdgcn_sched_barrier(0);
-            fold_stage<F, OP, M>(xa, acc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (k < n) {
-            if (k + 1 < n) {
-                load_stage<M, NT>(xa, p, off);
-                __builtin_amdgcn_sched_barrier(0);
-                fold_stage<F, OP, M>(xb, acc);
-                __builtin_amdgcn_sched_barrier(0);
-                fold_stage<F, OP, M>(xa, acc);
-            } else {
-                fold_stage<F, OP, M>(xb, acc);
-            }
-        }
+        fold_rank_major_any<F, OP, NT, M>(a.send, c, n, off, acc);
+        u32x4 xa[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
 #pragma unroll
@@ -1188,8 +1199,10 @@ __device__ __forceinline__ int multi_find_piece(cpiece* pieces, int npieces, uin
 // tensor (pointers) are uniform across the workgroup. A workgroup's tiles
 // only increase, so after a binary search for its first tile it finds the
 // next piece by scanning forward. NR > 0 fixes the rank count at compile time.
-// RM (with NR > 0) selects the rank-major vector tile: four kBlock-vector
-// quarters per tile, folded one rank at a time as in the flat rank-major body.
+// RM selects the rank-major vector tile, folded one rank at a time as in the
+// flat rank-major bodies: with NR > 0 four kBlock-vector quarters per tile;
+// with NR = 0 (above 8 ranks) rank_major_any_tiles quarters, folded by
+// fold_rank_major_any.
 template <class F, int OP, int NR, bool NT, bool RM = false>
 __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned char* table)
 {
@@ -1248,7 +1261,33 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
             const uint64_t boff = a0 * (16 / E);
             uint64_t vb, ve;
             piece_vectors(pc.j0, j_end, a0, E, &vb, &ve);
-            if constexpr (RM && NR > 0) {
+            if constexpr (RM && NR == 0) {
+                constexpr int M = rank_major_any_tiles(kRankMajorAnyMany, 16 / E);
+                const uint64_t v = vb + static_cast<uint64_t>(ti) * (M * kBlock) + threadIdx.x;
+                if (ve > vb) {
+                    // lanes past the piece read its first vector and drop it
+                    uint64_t off[M];
+                    bool ok[M];
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        ok[m] = v + m * kBlock < ve;
+                        off[m] = (ok[m] ? v + m * kBlock : vb) * 16 + boff;
+                    }
+                    Acc acc[M][E];
+                    fold_rank_major_any<F, OP, NT, M>(send, c, n, off, acc);
+                    u32x4 out[M];
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+#pragma unroll
+                        for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], n);
+                        out[m] = F::pack(acc[m]);
+                    }
+                    for (int r = 0; r < n; ++r)
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+                            if (ok[m]) stv_at<NT>(recv[r], off[m], out[m]);
+                }
+            } else if constexpr (RM && NR > 0) {
                 // the tile's four quarters: vectors v + m * kBlock of this
                 // thread; each stage loads them from one rank, the next
                 // rank's loads issued before the current rank's combine
@@ -1427,38 +1466,32 @@ hipError_t fused_nr(const ReduceArgs& a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
-// Tiles per super tile of the run-time rank-count rank-major kernel: 64 KiB
-// of fp32 per stage above 8 ranks and 16 KiB up to 8 (measured best of 2, 4,
-// 8 and 16 at 4-64 ranks); halved for 16-bit types, whose eight fp32
-// accumulators per vector would otherwise push the kernel past 128 VGPRs.
-template <class F>
-constexpr int rank_major_any_tiles(bool many)
-{
-    return (many ? 8 : 4) / (F::kEpv == 8 ? 2 : 1);
-}
-
-// The rank-major kernels: 16-byte vectors, non-temporal access, either
-// layout. 5..8 ranks take the fixed-rank-count body, other counts the
-// run-time one.
+// The rank-major kernels: 16-byte vectors, non-temporal access. The
+// all-reduce takes the run-time rank-count body at every rank count (at 5..8
+// ranks it ran level with the fixed-rank-count body from 128 MiB per rank
+// and 2-7% faster at 20-64 MiB); the reduce-scatter layout takes the
+// fixed-rank-count body at 5..8 ranks, the run-time one above.
 template <class F, int OP, bool SC>
 hipError_t fused_nr_rank_major(const ReduceArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 block(kBlock);
     constexpr int M = kRankMajorTiles;
-    switch (a.n) {
-    case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, M>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, M>), grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, M>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, M>), grid, block, 0, s, a); break;
-    default:
-        if (a.n > 8) {
-            constexpr int MA = rank_major_any_tiles<F>(true);
-            hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MA>), grid, block, 0, s, a);
-        } else {
-            constexpr int MA = rank_major_any_tiles<F>(false);
-            hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MA>), grid, block, 0, s, a);
+    constexpr int MA = rank_major_any_tiles(kRankMajorAnyMany, 16 / F::kEpv);
+    constexpr int MF = rank_major_any_tiles(kRankMajorAnyMany - 1, 16 / F::kEpv);
+    if (a.n > 8) {
+        hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MA>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    if constexpr (SC) {
+        switch (a.n) {
+        case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, M>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, M>), grid, block, 0, s, a); break;
+        case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, M>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, M>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MF>), grid, block, 0, s, a); break;
         }
-        break;
+    } else {
+        hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MF>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -1569,9 +1602,12 @@ hipError_t multi_nr(const MultiArgs& a, bool rank_major, int grid_x, hipStream_t
 {
     const dim3 grid(grid_x), block(kBlock);
     if (rank_major) {
-        // the rank-major kernel exists for 8 ranks with non-temporal access
-        if (!NT || a.h.n != 8) return hipErrorInvalidValue;
-        if constexpr (NT) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT, true>), grid, block, 0, s, a);
+        // the rank-major kernels: 8 ranks, or above 8, with non-temporal access
+        if (!NT || a.h.n < 8) return hipErrorInvalidValue;
+        if constexpr (NT) {
+            if (a.h.n == 8) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT, true>), grid, block, 0, s, a);
+        }
     } else if (a.h.n == 8) {
         hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);
     } else {

@@ -308,12 +308,65 @@ def test_bucket8_rank_major_multi_out_of_place():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("n,dtype,op,shift", [(17, "f32", "sum", 3), (17, "bf16", "avg", 0), (64, "f32", "min", 1),
+                                              (64, "f16", "max", 5), (24, "i32", "prod", 2)])
+def test_rank_major_any_multi_full_compare(n, dtype, op, shift):
+    """Above 8 ranks beyond the last-level cache the multi-tensor call takes
+    the rank-major tiles for run-time rank counts. Views of log-uniform sizes
+    into one allocation per rank, its base `shift` elements off a line, in
+    place: every element against the oracle's fold over the flat bucket, and
+    bit for bit against the flat call."""
+    e = gu.ESIZE[dtype]
+    count = ((5 << 20) if n > 32 else (20 << 20)) // e + 12_345
+    assert n * count * e > 256 << 20
+    sizes = synthetic.bucket_sizes(count, e, 4096, 64 << 20, seed=n)
+    flat_in = gu.make_inputs(n, count, dtype, op, seed=n + shift)
+    bufs = [gu.RankBuf(count, dtype, offset=shift * e) for _ in range(n)]
+    for r in range(n):
+        bufs[r].view.copy_(flat_in[r])
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    rows = [[bufs[r].sub_ptr(int(o)) for r in range(n)] for o in offs]
+    flat = [x.clone() for x in flat_in]
+    with ar.Comm(n, 0) as comm:
+        ar.ar_all_reduce_multi(comm, rows, rows, sizes, dtype, op)
+        fp = [b.data_ptr() for b in flat]
+        ar.ar_all_reduce(comm, fp, fp, count, dtype, op, "fused")
+        torch.cuda.synchronize()
+    exp = gu.oracle_all_reduce(flat_in, dtype, op)
+    for r in range(n):
+        assert bufs[r].guards_ok(), f"rank {r} guard"
+        got = gu.host(bufs[r].view)
+        gu.assert_same(got, exp[r], dtype, f"rank-major-any multi n={n} {dtype} {op} rank {r} vs oracle")
+        gu.assert_same(got, gu.host(flat[r]), dtype, f"rank-major-any multi n={n} {dtype} {op} rank {r} vs flat")
+    del flat_in, bufs, flat
+    torch.cuda.empty_cache()
+
+
+def test_rank_major_any_multi_out_of_place():
+    """The rank-major tiles for run-time rank counts with separate send and
+    recv allocations per tensor (fp16, 17 ranks, 23 MB per rank), tiny
+    tensors (no whole vector) among large ones: against the oracle."""
+    n, dtype = 17, "f16"
+    sizes = [1, 7, 9_000_000, 3, 4095, 1_500_001, 8, 900_000, 5]
+    assert 2 * n * sum(sizes) * 2 > 256 << 20
+    send, recv, exp = _multi_case(n, sizes, dtype, "sum", seed=79)
+    with ar.Comm(n, 0) as comm:
+        ar.ar_all_reduce_multi(comm, _ptrs(send), _ptrs(recv), sizes, dtype, "sum")
+        torch.cuda.synchronize()
+    _check_multi(recv, exp, dtype, "rank-major-any multi out of place")
+    for row in send + recv:
+        for b in row:
+            assert b.guards_ok()
+    del send, recv
+    torch.cuda.empty_cache()
+
+
 def _multi_case(n, sizes, dtype, op, seed):
     """Send tensors filled from a seeded flat bucket, empty recv tensors, and
     the oracle's flat-bucket result."""
     total = sum(sizes)
     flat = gu.make_inputs(n, total, dtype, op, seed=seed)
-    exp = oracle.fold_all_reduce([gu.host(x) for x in flat], dtype, op)
+    exp = gu.oracle_all_reduce(flat, dtype, op)
     send, recv, off = [], [], 0
     for c in sizes:
         row = [gu.RankBuf(c, dtype) for _ in range(n)]

@@ -1,7 +1,7 @@
-"""Streaming access (`ar_comm_set_streaming`): the one-launch calls take
-non-temporal loads and stores at sizes that fit the last-level cache. The
-results are the same bits as with the default cached access, and equal to
-the oracle's."""
+"""Access flavours (`ar_comm_set_access`, `ar_comm_set_streaming`): the
+one-launch calls with non-temporal loads and stores at sizes where the
+default would cache, and cached ones where it would stream. The results are
+the same bits either way, and equal to the oracle's."""
 import pytest
 
 import gpu_util as gu
@@ -75,3 +75,31 @@ def test_streaming_multi_tensor(n):
         ar.ar_comm_set_streaming(comm, True)
         check_multi(comm, sizes, "f32", "sum", seed=n + 40)
         check_multi(comm, sizes, "bf16", "max", seed=n + 41, inplace=True, offset=6)
+
+
+@pytest.mark.parametrize("n,dtype,op,count", [(8, "f32", "avg", 5_242_883), (4, "bf16", "sum", 20_971_529),
+                                              (8, "f16", "max", 8_388_611)])
+def test_access_flavours_agree(n, dtype, op, count):
+    """Footprints between half and all of the last-level cache, where the
+    default (AR_ACCESS_AUTO) all-reduce streams through the rank-major
+    kernels while AR_ACCESS_CACHED keeps cached two-tile kernels: auto,
+    streaming and cached give the same bits, equal to the oracle's, in place."""
+    xs = gu.make_inputs(n, count, dtype, op, seed=count % 89)
+    exp = gu.oracle_all_reduce(xs, dtype, op)
+    with ar.Comm(n, 0) as comm:
+        for access in ("auto", "streaming", "cached"):
+            ar.ar_comm_set_access(comm, access)
+            got, _, _ = gu.run_all_reduce(comm, xs, dtype, op, "fused", inplace=True)
+            for r in range(n):
+                gu.assert_same(got[r], exp[r], dtype, f"access={access} n={n} {dtype} {op} count={count} rank {r}")
+
+
+def test_access_rejects_unknown_values():
+    with ar.Comm(2, 0) as comm:
+        for bad in (-1, 3, 99):
+            with pytest.raises(ar.ArError) as ei:
+                ar.ar_comm_set_access(comm, bad)
+            assert ei.value.code == ar.AR_ERR_INVALID_ARGUMENT
+        ar.ar_comm_set_access(comm, "cached")
+        ar.ar_comm_set_streaming(comm, True)
+        ar.ar_comm_set_streaming(comm, False)
