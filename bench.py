@@ -344,6 +344,16 @@ def copy_probe(args, torch, ar):
                       "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "steps": args.steps}), flush=True)
 
 
+SWEEP_MODES = ("fused", "stepwise", "graph", "tree", "tree_stepwise")
+SWEEP_MARKER = "spin_kernel"  # torch.cuda._sleep's kernel: separates the sweep's groups in a kernel trace
+
+
+def sweep_launches(mode: str, n: int) -> int:
+    """Kernel launches one in-place all-reduce call makes in each mode."""
+    levels = (n - 1).bit_length()
+    return {"fused": 1, "tree": 1, "tree_stepwise": 2 * levels}.get(mode, 2 * (n - 1))
+
+
 def sweep(args, torch, ar, synthetic):
     """The alpha vs beta regimes: 8 ranks, 1 KiB .. 256 MiB per rank in powers
     of two, fp32 SUM, in place, each mode. One JSON line per (mode, size),
@@ -351,22 +361,39 @@ def sweep(args, torch, ar, synthetic):
     latency regime, beta from the HBM-bound sizes)
       ring modes: T = 2(N-1)*alpha + moved/beta, moved = 5(N-1)*S (the bytes
                   the N-1 reduce-scatter and N-1 all-gather steps move)
-      fused:      T = alpha + 2*N*S/beta."""
+      fused:      T = alpha + 2*N*S/beta.
+    The time per call is host events over back-to-back calls, so it includes
+    what the host spends enqueueing a call when that exceeds the device time.
+    Each (mode, size) group starts with a torch.cuda._sleep marker kernel, so
+    a rocprofv3 kernel trace of the run gives each group's device time
+    (--sweep-trace). --cold rotates buffer sets of at least 1 GiB so that
+    every call reads HBM; --sweep-iters caps the calls per group."""
     n = 8
     rows = []
+    group = 0
     with ar.Comm(n, 0) as comm:
         for log2 in range(10, 29):
             s_bytes = 1 << log2
             count = s_bytes // 4
-            bufs = synthetic.rank_inputs("sweep", n, count, "f32", device="cuda", salt=log2)
-            ptrs = [b.data_ptr() for b in bufs]
+            sets = -(-ROTATE_BYTES // (n * s_bytes)) if args.cold else 1
+            bufsets = [synthetic.rank_inputs("sweep", n, count, "f32", device="cuda", salt=log2 + 100 * k)
+                       for k in range(sets)]
+            ptrsets = [[b.data_ptr() for b in bufs] for bufs in bufsets]
             stream = torch.cuda.current_stream()
-            for mode in ("fused", "stepwise", "graph", "tree", "tree_stepwise"):
+            for mode in SWEEP_MODES:
+                cur = [0]
+
                 def call():
-                    ar.ar_all_reduce(comm, ptrs, ptrs, count, "f32", "sum", mode, stream)
+                    p = ptrsets[cur[0] % sets]
+                    cur[0] += 1
+                    ar.ar_all_reduce(comm, p, p, count, "f32", "sum", mode, stream)
+                torch.cuda.synchronize()
+                torch.cuda._sleep(1)  # group marker for kernel traces
                 for _ in range(5):
                     call()
                 iters = max(20, min(2000, int(2e9 / (2 * n * s_bytes))))
+                if args.sweep_iters:
+                    iters = min(iters, args.sweep_iters)
                 start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
                 start.record(stream)
@@ -375,10 +402,13 @@ def sweep(args, torch, ar, synthetic):
                 stop.record(stream)
                 torch.cuda.synchronize()
                 ms = start.elapsed_time(stop) / iters
+                calls = 5 + iters
                 # fused kinds read N*S and write N*S; the stepwise ring and
                 # tree both move 5(N-1)*S (3(N-1)S reducing, 2(N-1)S copying)
                 moved = 2 * n * s_bytes if mode in ("fused", "tree") else 5 * (n - 1) * s_bytes
-                row = {"sweep": mode, "bytes_per_rank": s_bytes, "us": round(ms * 1e3, 3), "iters": iters,
+                row = {"sweep": mode, "group": group, "bytes_per_rank": s_bytes, "us": round(ms * 1e3, 3),
+                       "iters": iters, "calls": calls, "launches_per_call": sweep_launches(mode, n),
+                       "rotating_buffer_sets": sets,
                        "algbw_gbps": round(s_bytes / (ms * 1e-3) / 1e9, 3),
                        "busbw_gbps": round(s_bytes / (ms * 1e-3) / 1e9 * 2 * (n - 1) / n, 3),
                        "moved_bytes": moved, "moved_gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
@@ -388,25 +418,74 @@ def sweep(args, torch, ar, synthetic):
                     steps = ar.ar_last_step_times_ms(comm)
                     ar.ar_comm_set_step_timing(comm, False)
                     row["step_us"] = [round(t * 1e3, 2) for t in steps]
+                    row["calls"] = calls + 1
                 rows.append(row)
+                group += 1
                 print(json.dumps(row), flush=True)
-            del bufs
+            del bufsets, ptrsets
             torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(1)  # closes the last group
+        torch.cuda.synchronize()
     fits = {}
-    levels = (n - 1).bit_length()
-    for mode in ("fused", "stepwise", "graph", "tree", "tree_stepwise"):
+    for mode in SWEEP_MODES:
         rs = [r for r in rows if r["sweep"] == mode]
-        launches = {"fused": 1, "tree": 1, "tree_stepwise": 2 * levels}.get(mode, 2 * (n - 1))
+        launches = sweep_launches(mode, n)
         alpha, beta = alpha_beta_fit([(r["bytes_per_rank"], r["moved_bytes"], r["us"] * 1e-6) for r in rs],
                                      launches, n)
         fits[mode] = {"alpha_us": round(alpha * 1e6, 3), "beta_gbps": round(beta / 1e9, 1) if beta else None,
                       "model": "T = %d*alpha + moved/beta" % launches,
                       "alpha_from": "sizes up to %d bytes per rank" % SWEEP_LATENCY_MAX,
                       "beta_from": "sizes with N*S above the %d MiB last-level cache" % (LLC_BYTES >> 20)}
-    small = {m: min(r["us"] for r in rows if r["sweep"] == m)
-             for m in ("fused", "stepwise", "graph", "tree", "tree_stepwise")}
-    print(json.dumps({"sweep_fit": fits, "smallest_call_us": small, "nranks": n, "dtype": "f32", "op": "sum"}),
-          flush=True)
+    small = {m: min(r["us"] for r in rows if r["sweep"] == m) for m in SWEEP_MODES}
+    print(json.dumps({"sweep_fit": fits, "smallest_call_us": small, "nranks": n, "dtype": "f32", "op": "sum",
+                      "cold": bool(args.cold)}), flush=True)
+
+
+def read_kernel_trace(path: str):
+    """(name, start ns, end ns) of every dispatch in a rocprofv3 kernel_trace.csv,
+    in start order."""
+    import csv
+    out = []
+    with open(path, newline="", encoding="utf-8") as f:
+        for rec in csv.DictReader(f):
+            out.append((rec["Kernel_Name"], int(rec["Start_Timestamp"]), int(rec["End_Timestamp"])))
+    out.sort(key=lambda x: x[1])
+    return out
+
+
+def sweep_trace_summary(trace, rows, nranks: int = 8):
+    """Each sweep group's device time from a kernel trace of the sweep: the
+    library's kernels (names in namespace ar::) between the group's marker and
+    the next one. Returns one dict per row with the kernel count found, the
+    expected count (calls x launches per call) and, when they agree, the
+    device time per call and per launch; plus the alpha-beta fits on device
+    time."""
+    groups, cur = [], None
+    for name, t0, t1 in trace:
+        if SWEEP_MARKER in name:
+            cur = []
+            groups.append(cur)
+        elif cur is not None and name.startswith("ar::"):
+            cur.append(t1 - t0)
+    out = []
+    for r in rows:
+        g = groups[r["group"]] if r["group"] < len(groups) else []
+        want = r["calls"] * r["launches_per_call"]
+        d = {"sweep": r["sweep"], "bytes_per_rank": r["bytes_per_rank"], "host_us": r["us"], "kernels": len(g),
+             "expected_kernels": want}
+        if len(g) == want and want:
+            d["device_us"] = sum(g) / r["calls"] / 1e3
+            d["device_us_per_launch"] = sum(g) / want / 1e3
+        out.append(d)
+    fits = {}
+    for mode in SWEEP_MODES:
+        pts = [(d["bytes_per_rank"], r["moved_bytes"], d["device_us"] * 1e-6)
+               for d, r in zip(out, rows) if d["sweep"] == mode and "device_us" in d]
+        if len(pts) == sum(1 for r in rows if r["sweep"] == mode) and pts:
+            alpha, beta = alpha_beta_fit(pts, sweep_launches(mode, nranks), nranks)
+            fits[mode] = {"alpha_device_us": alpha * 1e6, "beta_device_gbps": beta / 1e9 if beta else None}
+    return out, fits
 
 
 def main():
@@ -437,6 +516,14 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line, sweep 1 KiB .. 256 MiB per rank (8 ranks, fp32 SUM) in every "
                          "mode and fit the alpha-beta model")
+    ap.add_argument("--cold", action="store_true",
+                    help="with --sweep: rotate buffer sets of at least 1 GiB so every call reads HBM")
+    ap.add_argument("--sweep-iters", type=int, default=0, metavar="K",
+                    help="with --sweep: at most K timed calls per (mode, size) (for profiled runs)")
+    ap.add_argument("--sweep-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "SWEEP_JSONL"),
+                    help="instead of running anything, attribute a rocprofv3 kernel trace of a --sweep run to its "
+                         "(mode, size) groups and print each group's device time beside the host-event time, "
+                         "with alpha-beta fits on both")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the all-reduce, time a plain 16-byte-vector device copy of BYTES bytes "
                          "(a one-rank all-gather): the practical HBM ceiling, and the reference reading for "
@@ -448,6 +535,17 @@ def main():
               f"GPU as separate HBM buffers, and no figure across several GPUs is produced. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep_trace:
+        trace = read_kernel_trace(args.sweep_trace[0])
+        lines = [json.loads(ln) for ln in open(args.sweep_trace[1], encoding="utf-8") if ln.startswith("{")]
+        rows = [r for r in lines if "sweep" in r]
+        host_fit = next((r for r in lines if "sweep_fit" in r), None)
+        out, fits = sweep_trace_summary(trace, rows)
+        for d in out:
+            print(json.dumps(d), flush=True)
+        print(json.dumps({"device_fit": fits, "host_fit": host_fit["sweep_fit"] if host_fit else None}), flush=True)
+        return
 
     import torch
     import ring_all_reduce_ar_amd as ar

@@ -245,13 +245,14 @@ bool use_rank_major(size_t bytes_per_rank, int nranks, bool vec, bool nt)
     return nranks > 8 || bytes_per_rank <= (size_t(4) << 30);
 }
 
-// Workgroups per CU for the rank-major all-reduce: 32 from 32 ranks (64 ranks
-// x 256 MiB: 6.52 against 6.65 ms at 16; 32 ranks: 3.21 against 3.29 ms),
-// else 8 up to 32 MiB per rank (8 x 25 MiB cold: 73.2 against 76.6 us at 16)
-// and 16 above (8 x 64 MiB: 0.179 against 0.188 ms at 8).
+// Workgroups per CU for the rank-major all-reduce: 32 from 16 ranks (x 256 MiB
+// per rank, against 16: 64 ranks 6.52 / 6.65 ms, 32 ranks 3.21 / 3.29 ms, 16
+// ranks 1.59 / 1.63 ms), else 8 up to 32 MiB per rank (8 x 25 MiB cold: 73.2
+// against 76.6 us at 16) and 16 above (8 x 64 MiB: 0.179 against 0.188 ms
+// at 8).
 int rank_major_per_cu(int nranks, size_t bytes_per_rank)
 {
-    if (nranks >= 32) return 32;
+    if (nranks >= 16) return 32;
     return bytes_per_rank <= (size_t(32) << 20) ? 8 : 16;
 }
 
@@ -1171,8 +1172,8 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
     // 16 workgroups per CU: the 29-tensor 256 MiB bucket ran at 7.09 ms at 64
     // ranks (flat: 7.05) against 7.51 at 8 per CU, and 0.913 against 0.929 ms
     // at 8 ranks.
-    // The rank-major tiles above 32 ranks take 32 per CU, as the flat call.
-    const int cap = comm->num_cus * (rank_major && n > 32 ? 32 : 16);
+    // The rank-major tiles from 16 ranks take 32 per CU, as the flat call.
+    const int cap = comm->num_cus * (rank_major && n >= 16 ? 32 : 16);
 
     // The tables go in the kernel arguments, one launch per batch of tensors
     // that fits. (A table in device memory, written once and read by a single

@@ -88,3 +88,43 @@ def test_traffic_follows_collective_and_source_hash(monkeypatch, tmp_path):
     assert bench.load_traffic("w", "stepwise") is None
     monkeypatch.setattr(bench, "kernel_sha", lambda: "def456")
     assert bench.load_traffic("w", "fused") is None
+
+
+def test_sweep_trace_attribution(tmp_path):
+    """Each sweep group's library kernels are the ones between its marker
+    and the next; other kernels (torch's) are ignored; a group whose kernel
+    count differs from calls x launches gets no device time."""
+    rows = [
+        {"sweep": "fused", "group": 0, "bytes_per_rank": 1024, "us": 5.0, "calls": 3, "launches_per_call": 1,
+         "moved_bytes": 16 * 1024},
+        {"sweep": "stepwise", "group": 1, "bytes_per_rank": 1024, "us": 40.0, "calls": 2, "launches_per_call": 14,
+         "moved_bytes": 35 * 1024},
+        {"sweep": "tree", "group": 2, "bytes_per_rank": 1024, "us": 6.0, "calls": 2, "launches_per_call": 1,
+         "moved_bytes": 16 * 1024},
+    ]
+    t = 0
+    lines = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+
+    def k(name, dur):
+        nonlocal t
+        lines.append(f'"{name}",{t},{t + dur}')
+        t += dur + 10
+
+    k("at::native::uniform_kernel", 500)
+    k("spin_kernel(long)", 50)
+    for _ in range(3):
+        k("ar::detail::fused_reduce_vec<...>", 2000)
+    k("spin_kernel(long)", 50)
+    k("at::native::fill_kernel", 70)
+    for _ in range(2 * 14):
+        k("ar::detail::rs_step<...>", 1000)
+    k("spin_kernel(long)", 50)
+    k("ar::detail::tree_fused_vec<...>", 3000)  # one of two calls missing
+    k("spin_kernel(long)", 50)
+    path = tmp_path / "kernel_trace.csv"
+    path.write_text("\n".join(lines) + "\n")
+    out, _ = bench.sweep_trace_summary(bench.read_kernel_trace(str(path)), rows)
+    assert out[0]["kernels"] == 3 and abs(out[0]["device_us"] - 2.0) < 1e-9
+    assert out[1]["kernels"] == 28 and abs(out[1]["device_us"] - 14.0) < 1e-9
+    assert abs(out[1]["device_us_per_launch"] - 1.0) < 1e-9
+    assert out[2]["kernels"] == 1 and "device_us" not in out[2]
