@@ -345,6 +345,7 @@ def copy_probe(args, torch, ar):
 
 
 SWEEP_MODES = ("fused", "stepwise", "graph", "tree", "tree_stepwise")
+SWEEP_MAX_SETS = 64
 SWEEP_MARKER = "spin_kernel"  # torch.cuda._sleep's kernel: separates the sweep's groups in a kernel trace
 
 
@@ -366,8 +367,9 @@ def sweep(args, torch, ar, synthetic):
     what the host spends enqueueing a call when that exceeds the device time.
     Each (mode, size) group starts with a torch.cuda._sleep marker kernel, so
     a rocprofv3 kernel trace of the run gives each group's device time
-    (--sweep-trace). --cold rotates buffer sets of at least 1 GiB so that
-    every call reads HBM; --sweep-iters caps the calls per group."""
+    (--sweep-trace). --cold rotates buffer sets of at least 1 GiB (at most
+    SWEEP_MAX_SETS sets) so that every call reads HBM; --sweep-iters caps the
+    calls per group."""
     n = 8
     rows = []
     group = 0
@@ -375,7 +377,9 @@ def sweep(args, torch, ar, synthetic):
         for log2 in range(10, 29):
             s_bytes = 1 << log2
             count = s_bytes // 4
-            sets = -(-ROTATE_BYTES // (n * s_bytes)) if args.cold else 1
+            # at most SWEEP_MAX_SETS sets: below 2 MiB per rank the rotation
+            # covers less than 1 GiB and the calls are partly cache-resident
+            sets = min(SWEEP_MAX_SETS, -(-ROTATE_BYTES // (n * s_bytes))) if args.cold else 1
             bufsets = [synthetic.rank_inputs("sweep", n, count, "f32", device="cuda", salt=log2 + 100 * k)
                        for k in range(sets)]
             ptrsets = [[b.data_ptr() for b in bufs] for bufs in bufsets]
@@ -457,7 +461,7 @@ def read_kernel_trace(path: str):
 def sweep_trace_summary(trace, rows, nranks: int = 8):
     """Each sweep group's device time from a kernel trace of the sweep: the
     library's kernels (names in namespace ar::) between the group's marker and
-    the next one. Returns one dict per row with the kernel count found, the
+    the next one (rocprofv3 prints them as "void ar::..."). Returns one dict per row with the kernel count found, the
     expected count (calls x launches per call) and, when they agree, the
     device time per call and per launch; plus the alpha-beta fits on device
     time."""
@@ -466,7 +470,7 @@ def sweep_trace_summary(trace, rows, nranks: int = 8):
         if SWEEP_MARKER in name:
             cur = []
             groups.append(cur)
-        elif cur is not None and name.startswith("ar::"):
+        elif cur is not None and (name.startswith("ar::") or name.startswith("void ar::")):
             cur.append(t1 - t0)
     out = []
     for r in rows:

@@ -111,9 +111,9 @@ def test_sweep_trace_attribution(tmp_path):
         t += dur + 10
 
     k("at::native::uniform_kernel", 500)
-    k("spin_kernel(long)", 50)
+    k("at::cuda::(anonymous namespace)::spin_kernel(long)", 50)
     for _ in range(3):
-        k("ar::detail::fused_reduce_vec<...>", 2000)
+        k("void ar::detail::fused_reduce_vec<...>(ar::ReduceArgs)", 2000)
     k("spin_kernel(long)", 50)
     k("at::native::fill_kernel", 70)
     for _ in range(2 * 14):
