@@ -39,6 +39,9 @@ Reported (one JSON line):
   copy_ceiling a plain 1 GiB device copy timed in the same process: the
                practical read-once write-once rate of this machine, and the
                call's rate over it
+  same_buffer_copy (all-reduce) a plain copy of each rank buffer into the
+               next one, on the call's own allocations: the same bytes as the
+               call, and the call's rate over it
   cpu_baseline the CPU oracle on the workload, or a window of it, in the same
                unit: the literal ring on the host's threads (OMP_NUM_THREADS,
                else the affinity mask), and beside it the per-element fold
@@ -297,6 +300,7 @@ def range_point(torch, ar, synthetic, name: str, steps: int, warmup: int, copy_g
                 ar.ar_all_reduce(comm, p, p, count, dtype, op, "fused", stream)
 
             times.append(time_steps(torch, stream, step, steps, warmup)[0])
+            sb_ms = same_buffer_copy_ms(torch, ar, ptrsets[0], s_bytes, stream) if s_bytes % 16 == 0 else None
             del bufsets, ptrsets
             torch.cuda.empty_cache()
     ms = times[1]
@@ -306,7 +310,35 @@ def range_point(torch, ar, synthetic, name: str, steps: int, warmup: int, copy_g
             "steps": steps, "rotating_buffer_sets": sets, "ms_per_step": sig(ms),
             "first_allocation_ms_per_step": sig(times[0]), "algbw_gbps": sig(algbw),
             "busbw_gbps": sig(algbw * 2 * (n - 1) / n), "hbm_gbps": sig(alg),
-            "hbm_frac": sig(alg / HBM_PEAK_GBPS), "achieved_over_copy": sig(alg / copy_gbps)}
+            "hbm_frac": sig(alg / HBM_PEAK_GBPS), "achieved_over_copy": sig(alg / copy_gbps),
+            "same_buffer_copy": None if sb_ms is None else {
+                "ms": sig(sb_ms), "hbm_frac": sig(2 * n * s_bytes / (sb_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS),
+                "achieved_over_copy": sig(sb_ms / ms)}}
+
+
+def same_buffer_copy_ms(torch, ar, ptrs, nbytes: int, stream, steps: int = 5):
+    """A plain copy on the call's own rank buffers: rank r's buffer into rank
+    r+1's, for every r (one-rank all-gathers, 16-byte vectors), so every
+    buffer is read once and written once, 2*N*nbytes in all, the all-reduce's
+    bytes on the same allocations. Overwrites the buffers. Returns ms per
+    pass over the N buffers (best of `steps`)."""
+    n = len(ptrs)
+    best = None
+    with ar.Comm(1, 0) as comm:
+        def one():
+            for r in range(n):
+                ar.ar_all_gather(comm, [ptrs[r]], [ptrs[(r + 1) % n]], nbytes // 4, "i32", "fused", stream)
+        one()
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            one()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1)
+            best = t if best is None else min(best, t)
+    return best
 
 
 def time_copy(torch, ar, nbytes: int, steps: int, warmup: int):
@@ -662,10 +694,14 @@ def main():
                 calls.append(ar.ar_last_step_times_ms(comm))
             ar.ar_comm_set_step_timing(comm, False)
             ring_steps = calls
+        sbc = None
+        if measure_warm and coll == "all_reduce" and sizes is None and s_bytes % 16 == 0:
+            # the same bytes as a plain copy on these rank buffers (overwrites them)
+            sbc = same_buffer_copy_ms(torch, ar, ptrsets[0], s_bytes, stream, steps=3)
         ar.ar_comm_set_workspace(comm, None)
         del bufsets, ptrsets, outsets, outptrs, ws
         torch.cuda.empty_cache()
-        return ms_, per_step, warm, ring_steps
+        return ms_, per_step, warm, ring_steps, sbc
 
     # The first allocation of the rank buffers in a fresh process measured up
     # to ~9% slower on MI355X than the same buffers allocated again after a
@@ -673,7 +709,7 @@ def main():
     # are timed; the second is the steady state a long-running job sees and
     # is the reported value; the first is reported beside it.
     first_ms = timed_pass(False)[0]
-    ms, per_step, warm_ms, ring_steps = timed_pass(True)
+    ms, per_step, warm_ms, ring_steps, sbc_ms = timed_pass(True)
     per_step.sort()
 
     # nccl-tests conventions: algbw = S / T with S the per-rank buffer of
@@ -734,6 +770,13 @@ def main():
     result["copy_ceiling"] = {"bytes": COPY_CEILING_BYTES, "ms": sig(cms), "hbm_gbps": sig(cgbps),
                               "hbm_frac": sig(cgbps / HBM_PEAK_GBPS),
                               "achieved_over_copy": sig(achieved / cgbps)}
+    if sbc_ms:
+        # a copy that reads and writes each of the call's own rank buffers once
+        # (rank r into rank r+1): the all-reduce's bytes on the same
+        # allocations, whose placement in memory sets the rate of both
+        result["same_buffer_copy"] = {"ms": sig(sbc_ms), "hbm_frac": sig(alg_bytes / (sbc_ms * 1e-3) / 1e9 /
+                                                                          HBM_PEAK_GBPS),
+                                      "achieved_over_copy": sig(sbc_ms / ms)}
     if ring_steps:
         # Per-launch device times of the ring (the alpha-beta model's steps:
         # geek-doc page "训练梯度同步与集合通信", section 四; handbook

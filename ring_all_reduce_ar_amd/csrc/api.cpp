@@ -232,28 +232,45 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
     return f;
 }
 
-// The rank-major all-reduce kernels (16-byte vectors, non-temporal access)
-// whenever the call streams: up to 4 GiB per rank at 4..8 ranks, at every
-// size above 8 ranks. Measured against the kernels used before on the same
-// buffers (fp32): at 8 ranks +15% cold at 20-32 MiB per rank, +10% at 64
-// and 128 MiB, +2.4 to +3.5 points at 256 MiB, about +0.5 at 1-4 GiB, -1.1
-// to +0.6 at 14 GB (hence the 4 GiB bound); at 4 ranks +16% cold at 40 MiB
-// and +6.6% at 256 MiB; above 8 ranks see fused_rank_major_any.
-bool use_rank_major(size_t bytes_per_rank, int nranks, bool vec, bool nt)
+// The rank-major all-reduce kernel (16-byte vectors, non-temporal access)
+// whenever the call streams, from 4 ranks. Measured against the kernels used
+// before on the same buffers (fp32 unless noted): at 8 ranks +15% cold at
+// 20-32 MiB per rank, +10% at 64 and 128 MiB, +5% at 256 MiB, +7.5% at
+// 1 GiB, +3.6% at 4 GiB, +3% at 14 GB fp16 (with one super tile per
+// workgroup, rank_major_grid); at 4 ranks +16% cold at 40 MiB and +6.6% at
+// 256 MiB; above 8 ranks see fused_rank_major_any.
+bool use_rank_major(int nranks, bool vec, bool nt) { return vec && nt && nranks >= 4; }
+
+// Workgroups per chunk row for the rank-major all-reduce: one per super tile
+// (rank_major_any_tiles tiles of kBlock 16-byte vectors), so no workgroup
+// strides through its row. The hardware dispatches workgroups in order, so
+// the resident ones work through one chunk row after another, each on its
+// own contiguous super tile. Against a grid-stride grid of 16 workgroups
+// per CU on the same buffers: 8 x 256 MiB 0.755 / 0.793 ms, 8 x 1 GiB 3.00 /
+// 3.22 ms, 8 x 4 GiB 12.64 / 13.10 ms, 8 x 7e9 fp16 36.9 / 38.0 ms (there
+// against the two-tile kernel). The count is an upper bound on every row's
+// super tiles (a chunk's first tile may start before it); extra workgroups
+// find no super tile and exit. The kernels stride by the grid, so a row of
+// more than kMaxGridX super tiles (chunks beyond 64 GiB) stays correct.
+constexpr uint64_t kMaxGridX = (uint64_t(1) << 32) / ar::kBlock - 1;  // work-items per dimension fit 32 bits
+
+int rank_major_grid(uint64_t q, size_t elem, int nranks)
 {
-    if (!vec || !nt || nranks < 4) return false;
-    return nranks > 8 || bytes_per_rank <= (size_t(4) << 30);
+    const uint64_t tiles = ceil_div(ceil_div(q, 16 / elem), static_cast<uint64_t>(ar::kBlock)) + 1;
+    const uint64_t m = static_cast<uint64_t>(ar::rank_major_any_tiles(nranks, static_cast<int>(elem)));
+    return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, m), 1, kMaxGridX));
 }
 
-// Workgroups per CU for the rank-major all-reduce: 32 from 16 ranks (x 256 MiB
-// per rank, against 16: 64 ranks 6.52 / 6.65 ms, 32 ranks 3.21 / 3.29 ms, 16
-// ranks 1.59 / 1.63 ms), else 8 up to 32 MiB per rank (8 x 25 MiB cold: 73.2
-// against 76.6 us at 16) and 16 above (8 x 64 MiB: 0.179 against 0.188 ms
-// at 8).
-int rank_major_per_cu(int nranks, size_t bytes_per_rank)
+// The same for the reduce-scatter layout, whose tiles count from the chunk
+// start (block c of the output): the fixed-rank-count body at 5..8 ranks
+// takes kRankMajorTiles tiles per super tile, the run-time one
+// rank_major_any_tiles.
+int rank_major_scatter_grid(uint64_t q, size_t elem, int nranks)
 {
-    if (nranks >= 16) return 32;
-    return bytes_per_rank <= (size_t(32) << 20) ? 8 : 16;
+    const uint64_t tiles = ceil_div(ceil_div(q, 16 / elem), static_cast<uint64_t>(ar::kBlock));
+    const uint64_t m = nranks > 8 ? static_cast<uint64_t>(ar::rank_major_any_tiles(nranks, static_cast<int>(elem)))
+                                  : static_cast<uint64_t>(ar::kRankMajorTiles);
+    return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, m), 1, kMaxGridX));
 }
 
 // The multi-tensor call's rank-major tiles beyond the last-level cache: at 8
@@ -716,9 +733,9 @@ ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* 
         a.q = q;
         a.n = n;
         const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, bytes, bytes), kAllReduceStreamBytes);
-        const bool rank_major = use_rank_major(bytes, n, vec, nt);
-        const int gx = grid_for(comm, vec ? ceil_div(q, epv) : q, n,
-                                rank_major ? rank_major_per_cu(n, bytes) : fused_per_cu(bytes, n, !nt));
+        const bool rank_major = use_rank_major(n, vec, nt);
+        const int gx = rank_major ? rank_major_grid(q, e, n)
+                                  : grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n, !nt));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rank_major, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -835,16 +852,15 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.q = q;
         a.n = n;
         const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, sbytes, rbytes), kLastLevelCacheBytes);
-        // Rank-major kernels beyond the last-level cache from 5 ranks up: at
-        // 5..8 ranks 16 workgroups per CU up to 4 GiB of input per rank, 8
-        // above (+9 points at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against
-        // the two-tile kernels on the same buffers); above 8 ranks the
-        // run-time rank-count body, as the all-reduce takes it.
+        // Rank-major kernels beyond the last-level cache from 5 ranks up, one
+        // workgroup per super tile (+9 points at 256 MiB, +3.7 at 1 GiB, +1.5
+        // at 14 GB against the two-tile kernels on the same buffers with 8-16
+        // workgroups per CU; the exact grid then took 8 x 7e9 fp16 from 21.86
+        // to 20.85 ms and 8 x 64 MiB fp32 from 0.407 to 0.397 ms); above 8
+        // ranks the run-time rank-count body, as the all-reduce takes it.
         const bool rank_major = vec && nt && n >= 5;
-        const int per_cu = !rank_major ? (n <= 2 ? 4 : 8)
-                           : n > 8    ? rank_major_per_cu(n, sbytes)
-                                      : (sbytes <= (size_t(4) << 30) ? 16 : 8);
-        const int gx_f = grid_for(comm, vec ? ceil_div(q, epv) : q, n, per_cu);
+        const int gx_f = rank_major ? rank_major_scatter_grid(q, e, n)
+                                    : grid_for(comm, vec ? ceil_div(q, epv) : q, n, n <= 2 ? 4 : 8);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, rank_major, gx_f, s);
             return err != hipSuccess ? err : tick(t);

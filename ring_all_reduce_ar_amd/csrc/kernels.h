@@ -119,6 +119,10 @@ constexpr int kMultiBlobBytes = 3840;
 constexpr int kMultiVecTile = 2 * kBlock;
 constexpr int kMultiRankMajorTile = 4 * kBlock;
 
+// Tiles a thread of the fixed-rank-count rank-major kernels (reduce-scatter at
+// 5..8 ranks, the rank-major all-gather copy) takes together.
+constexpr int kRankMajorTiles = 4;
+
 // Tiles (of kBlock 16-byte vectors) per super tile of the rank-major kernels
 // for run-time rank counts: 8 above 8 ranks and 4 up to 8 for 4-byte types
 // (64 and 16 KiB per rank and stage; measured best of 2, 4, 8 and 16 at
@@ -166,8 +170,10 @@ hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hi
 // has checked that every rank pointer is 16-byte aligned, and for the
 // reduce-scatter layout also q % (16/elem) == 0); `nt` selects non-temporal
 // loads and stores (footprints beyond the last-level cache) over cached ones;
-// `rank_major` selects the rank-major kernels (needs vec, nt and 5..8
-// ranks).
+// `rank_major` selects the rank-major kernels (needs vec and nt; the
+// reduce-scatter layout also 5 ranks or more). Any grid is correct (the
+// kernels stride by it); the rank-major ones run best with one workgroup per
+// super tile.
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
                                bool rank_major, int grid_x, hipStream_t stream);
 

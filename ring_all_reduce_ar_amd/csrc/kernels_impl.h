@@ -384,8 +384,6 @@ __device__ __forceinline__ void fused_x2(const ReduceArgs& a, int c, uint64_t or
     }
 }
 
-// Tiles a rank-major thread folds together.
-constexpr int kRankMajorTiles = 4;
 
 // Rank-major body of the fused reduction (NR ranks known at compile time): a
 // thread takes M consecutive tiles per grid-stride step and folds them one
@@ -397,12 +395,13 @@ constexpr int kRankMajorTiles = 4;
 // waves of the CU (96 VGPRs: five per SIMD) cover the latency. A variant
 // with a real prefetch distance of 1-3 stages held 120-130 VGPRs and ran
 // 2-6% slower at 8 ranks x 64 MiB-1 GiB. Then the M results go to every rank
-// (all-reduce) or to the chunk's output block (SCATTER). Each element's fold is the ring order of
-// the two-tile body. Measured against the two-tile body on the same buffers
-// at 5-8 ranks: all-reduce +2.4 to +3.5 points at 256 MiB per rank, about
-// +0.5 at 1-4 GiB, -1.1 to +0.6 at 14 GB (so it stops at 4 GiB);
-// reduce-scatter +9 points at 256 MiB in per rank, +3.7 at 1 GiB, +1.5 at
-// 14 GB (at 8 workgroups per CU).
+// (all-reduce) or to the chunk's output block (SCATTER). Each element's fold
+// is the ring order of the two-tile body. The reduce-scatter takes it at 5-8
+// ranks: +9 points at 256 MiB in per rank, +3.7 at 1 GiB, +1.5 at 14 GB
+// against the two-tile body on the same buffers (at 8 workgroups per CU).
+// The all-reduce takes the pipelined run-time body below at every rank
+// count, which measured faster than this one at 8 ranks once launched with
+// one workgroup per super tile.
 template <class F, int OP, int NR, bool NT, int M, bool SCATTER = false>
 __device__ __forceinline__ void fused_rank_major(const ReduceArgs& a, int c, uint64_t org, uint64_t v0, uint64_t v1,
                                                  uint64_t ntiles, uint64_t rot)

@@ -62,6 +62,8 @@ def test_bench_line_sweep_point(mode):
     assert j["dtype"] == "f32" and j["config"]["mode"] == mode
     # the counter traffic appears only while the sources match its summary
     assert j["roofline"]["traffic"] == bench.load_traffic("sweep256m", mode)
+    sb = j["same_buffer_copy"]
+    assert sb["achieved_over_copy"] == pytest.approx(sb["ms"] / j["ms_per_step"], rel=1e-3)
     if mode == "stepwise":
         mv = j["moved"]
         assert mv["bytes"] == bench.ring_moved_bytes(n, j["config"]["count_per_rank"], "f32")
@@ -105,3 +107,6 @@ def test_range_point_fields():
     assert p["hbm_frac"] == pytest.approx(p["hbm_gbps"] / 8000.0, abs=1e-4)
     assert p["achieved_over_copy"] == pytest.approx(p["hbm_gbps"] / 4000.0, rel=1e-3)
     assert p["first_allocation_ms_per_step"] > 0
+    sb = p["same_buffer_copy"]
+    assert sb["ms"] > 0 and sb["achieved_over_copy"] == pytest.approx(sb["ms"] / p["ms_per_step"], rel=1e-3)
+    assert sb["hbm_frac"] == pytest.approx(2 * n * S / (sb["ms"] * 1e-3) / 8e12, rel=2e-3)

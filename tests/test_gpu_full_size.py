@@ -236,8 +236,9 @@ def test_odd_rank_counts_large(n, count, dtype):
 
 def _generic_case(n, dtype, extra):
     # chunk length giving each chunk row 2G + G/3 + 1 tiles of 4 KiB, G being
-    # the row's workgroups at 16 per CU (the 5..64-rank rule up to 128 MiB
-    # per rank), plus `extra` elements so chunks start inside a vector
+    # 16 workgroups per CU over the n rows (a tile count that is no multiple
+    # of the kernels' super tiles), plus `extra` elements so chunks start
+    # inside a vector
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     g = max(1, cus * 16 // n)
     tiles = 2 * g + g // 3 + 1
@@ -271,10 +272,11 @@ def test_generic_rank_counts_full_compare(n, dtype, op, extra):
     (8, "f16", "prod", 67_108_880, True),
 ])
 def test_rank_major_range_full_compare(n, dtype, op, count, inplace):
-    """Just above 128 MiB per rank at 5-8 ranks the all-reduce takes its
-    rank-major kernels (a thread folds four consecutive tiles one rank at a
-    time): every element of every rank against the oracle, with ragged chunks
-    and guard bands."""
+    """Once the all-reduce streams (footprints above half the last-level
+    cache, as all of these) it takes its rank-major kernel from 4 ranks (a
+    thread folds consecutive tiles one rank at a time, one workgroup per
+    super tile): every element of every rank against the oracle, with ragged
+    chunks and guard bands."""
     with ar.Comm(n, 0) as comm:
         xs = gu.make_inputs(n, count, dtype, op, seed=count % 1000)
         exp = gu.oracle_all_reduce(xs, dtype, op)
@@ -286,11 +288,12 @@ def test_rank_major_range_full_compare(n, dtype, op, count, inplace):
 
 
 def _rank_major_any_case(n, dtype, extra):
-    # chunk rows of G + G/3 super tiles plus one tile, G being the row's
-    # workgroups (16 per CU, 32 above 32 ranks) and a super tile M tiles of
-    # 4 KiB (8 above 8 ranks, 4 up to 8, halved for 16-bit types): a full
-    # grid-stride pass, a second for a third of the workgroups, a last super
-    # tile holding one tile; `extra` elements make chunks start inside a vector
+    # chunk rows of G + G/3 super tiles plus one tile (G a few hundred, from
+    # the CU count), a super tile being M tiles of 4 KiB (8 above 8 ranks, 4
+    # up to 8, halved for 16-bit types): the launch has one workgroup per
+    # super tile, the last of which holds one tile, and every chunk after the
+    # first starts inside a tile; `extra` elements make chunks start inside a
+    # vector
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     g = max(1, cus * (32 if n > 32 else 16) // n)
     m = (8 if n > 8 else 4) // (2 if gu.ESIZE[dtype] == 2 else 1)
@@ -308,8 +311,8 @@ def _rank_major_any_case(n, dtype, extra):
 ])
 def test_rank_major_any_full_compare(n, dtype, op, extra, inplace):
     """The rank-major kernel for run-time rank counts (4 ranks and above 8,
-    beyond the last-level cache): several grid-stride passes per chunk row,
-    a partial last super tile, ragged chunks; every element of every rank
+    beyond the last-level cache): hundreds of super tiles per chunk row, a
+    partial last super tile, ragged chunks; every element of every rank
     against the oracle, with guard bands."""
     count = _rank_major_any_case(n, dtype, extra)
     with ar.Comm(n, 0) as comm:
@@ -339,9 +342,10 @@ def test_rank_major_from_64mib_full_compare(n, dtype, op, count):
 
 @pytest.mark.parametrize("n,count,dtype", [(8, 1 << 30, "f32"), (8, (1 << 31) - 5, "f16"), (6, 999_999_997, "f32")])
 def test_rank_major_upper_sizes_sampled(n, count, dtype):
-    """At and below the rank-major kernels' 4 GiB-per-rank bound, in place as
-    the benchmark launches them: sampled elements (every chunk boundary
-    among them) against the oracle, all ranks identical."""
+    """The rank-major all-reduce at 2.4-4 GiB per rank, in place as the
+    benchmark launches it (one workgroup per super tile, over a hundred
+    thousand workgroups): sampled elements (every chunk boundary among them)
+    against the oracle, all ranks identical."""
     with ar.Comm(n, 0) as comm:
         bufs = synthetic.rank_inputs("sweep", n, count, dtype, device="cuda", salt=7)
         check_sampled(comm, bufs, dtype, "sum", "fused", seed=n)

@@ -82,7 +82,7 @@ def test_streaming_multi_tensor(n):
 def test_access_flavours_agree(n, dtype, op, count):
     """Footprints between half and all of the last-level cache, where the
     default (AR_ACCESS_AUTO) all-reduce streams through the rank-major
-    kernels while AR_ACCESS_CACHED keeps cached two-tile kernels: auto,
+    kernel while AR_ACCESS_CACHED keeps cached two-tile kernels: auto,
     streaming and cached give the same bits, equal to the oracle's, in place."""
     xs = gu.make_inputs(n, count, dtype, op, seed=count % 89)
     exp = gu.oracle_all_reduce(xs, dtype, op)
