@@ -273,13 +273,9 @@ int rank_major_scatter_grid(uint64_t q, size_t elem, int nranks)
     return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, m), 1, kMaxGridX));
 }
 
-// The multi-tensor call's rank-major tiles beyond the last-level cache: at 8
-// ranks for 128 MiB-4 GiB of bucket per rank, above 8 ranks at every size.
-bool use_rank_major_multi(size_t bytes_per_rank, int nranks, bool nt)
-{
-    if (!nt || nranks < 8) return false;
-    return nranks > 8 || (bytes_per_rank > (size_t(128) << 20) && bytes_per_rank <= (size_t(4) << 30));
-}
+// The multi-tensor call's rank-major tiles whenever the call streams, from 4
+// ranks, as the flat all-reduce.
+bool use_rank_major_multi(int nranks, bool nt) { return nt && nranks >= 4; }
 
 // Workgroups per CU for the fused all-reduce, from sweeps of 2..16 per CU in
 // one process on MI355X (fp32 SUM, 64 MiB..1 GiB per rank, N = 2..64; fp16
@@ -1135,14 +1131,13 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
     uint64_t touched = 0;
     for (const Interval& x : iv) touched += x.hi - x.lo;
     const bool nt = call_nt(comm, touched, kAllReduceStreamBytes);
-    // The rank-major kernels (use_rank_major_multi: the bucket's bytes per
-    // rank); their vector tiles are four kBlock-vector quarters wide at 8
-    // ranks, rank_major_any_tiles quarters above.
-    const bool rank_major = use_rank_major_multi(total * e, n, nt);
-    const uint64_t tile_vecs = !rank_major ? ar::kMultiVecTile
-                               : n == 8   ? ar::kMultiRankMajorTile
-                                          : static_cast<uint64_t>(ar::rank_major_any_tiles(n, static_cast<int>(e))) *
-                                                ar::kBlock;
+    // The rank-major kernel (use_rank_major_multi) cuts vector pieces into
+    // tiles of rank_major_any_tiles quarters, as the flat kernel's super
+    // tiles.
+    const bool rank_major = use_rank_major_multi(n, nt);
+    const uint64_t tile_vecs =
+        rank_major ? static_cast<uint64_t>(ar::rank_major_any_tiles(n, static_cast<int>(e))) * ar::kBlock
+                   : static_cast<uint64_t>(ar::kMultiVecTile);
 
     // Lays out tensors [t0, t1) of the plan as one table (pointer blocks,
     // then pieces with their first tiles) and returns its header.
@@ -1185,11 +1180,17 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
         return bytes;
     };
 
-    // 16 workgroups per CU: the 29-tensor 256 MiB bucket ran at 7.09 ms at 64
-    // ranks (flat: 7.05) against 7.51 at 8 per CU, and 0.913 against 0.929 ms
-    // at 8 ranks.
-    // The rank-major tiles from 16 ranks take 32 per CU, as the flat call.
-    const int cap = comm->num_cus * (rank_major && n >= 16 ? 32 : 16);
+    // The two-tile kernel: at most 16 workgroups per CU (the 29-tensor
+    // 256 MiB bucket ran at 7.09 ms at 64 ranks against 7.51 at 8 per CU, and
+    // 0.913 against 0.929 ms at 8 ranks). The rank-major kernel: one
+    // workgroup per tile, taken in order, as the flat call's super tiles.
+    // Against the kernels used before on the same buffers (grid-stride, 16-32
+    // per CU, tiles interleaved over N segments; a fixed-rank-count tile at 8
+    // ranks; the two-tile kernel below 8 ranks and below 128 MiB per rank at
+    // 8), fp32 MAX as 29 tensors: 64 x 256 MiB 6.82 -> 6.57 ms, 8 x
+    // 256 MiB 0.802 -> 0.753 ms, 4 x 256 MiB 0.398 -> 0.366 ms; as 10
+    // tensors 8 x 64 MiB 0.205 -> 0.183 ms, 8 x 25 MiB 80.7 -> 74.2 us.
+    const int cap = comm->num_cus * 16;
 
     // The tables go in the kernel arguments, one launch per batch of tensors
     // that fits. (A table in device memory, written once and read by a single
@@ -1211,9 +1212,9 @@ AR_EXPORT ar_result_t ar_all_reduce_multi(ar_comm_t comm, int ntensors, const vo
                      n, plan.size(), dtype_name(dtype), static_cast<int>(op), batches.size(), rank_major ? 1 : 0);
     return run_eager(comm, stream, static_cast<int>(batches.size()), [&](hipStream_t s, StepTimer* t) {
         for (const auto& a : batches) {
-            hipError_t e2 =
-                ar::launch_multi_reduce(a, dtype, op, nt, rank_major,
-                                        static_cast<int>(std::min<uint64_t>(a.h.ntiles, cap)), s);
+            const uint64_t gx = rank_major ? std::min<uint64_t>(a.h.ntiles, kMaxGridX)
+                                           : std::min<uint64_t>(a.h.ntiles, cap);
+            hipError_t e2 = ar::launch_multi_reduce(a, dtype, op, nt, rank_major, static_cast<int>(gx), s);
             if (e2 == hipSuccess) e2 = tick(t);
             if (e2 != hipSuccess) return e2;
         }

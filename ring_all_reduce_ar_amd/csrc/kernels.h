@@ -114,10 +114,9 @@ struct MultiPiece {
 static_assert(sizeof(MultiPiece) == 24, "MultiPiece layout");
 constexpr int kMultiBlobBytes = 3840;
 // Vector pieces are cut into tiles of two kBlock-vector halves (a thread
-// takes one vector in each), or of four for the rank-major kernel; element
-// pieces into tiles of kBlock elements.
+// takes one vector in each), or of rank_major_any_tiles for the rank-major
+// kernel; element pieces into tiles of kBlock elements.
 constexpr int kMultiVecTile = 2 * kBlock;
-constexpr int kMultiRankMajorTile = 4 * kBlock;
 
 // Tiles a thread of the fixed-rank-count rank-major kernels (reduce-scatter at
 // 5..8 ranks, the rank-major all-gather copy) takes together.
@@ -147,9 +146,9 @@ struct MultiArgs {
     alignas(16) unsigned char blob[kMultiBlobBytes];
 };
 
-// `rank_major` selects the rank-major kernel (needs nt and at least 8 ranks;
-// the table's vector tiles are then kMultiRankMajorTile vectors wide at 8
-// ranks, rank_major_any_tiles(n, elem) * kBlock above).
+// `rank_major` selects the rank-major kernel (needs nt and at least 4 ranks;
+// the table's vector tiles are then rank_major_any_tiles(n, elem) * kBlock
+// vectors wide).
 hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op, bool nt, bool rank_major, int grid_x,
                                hipStream_t stream);
 

@@ -1198,23 +1198,24 @@ __device__ __forceinline__ int multi_find_piece(cpiece* pieces, int npieces, uin
 // tensor (pointers) are uniform across the workgroup. A workgroup's tiles
 // only increase, so after a binary search for its first tile it finds the
 // next piece by scanning forward. NR > 0 fixes the rank count at compile time.
-// RM selects the rank-major vector tile, folded one rank at a time as in the
-// flat rank-major bodies: with NR > 0 four kBlock-vector quarters per tile;
-// with NR = 0 (above 8 ranks) rank_major_any_tiles quarters, folded by
-// fold_rank_major_any.
-template <class F, int OP, int NR, bool NT, bool RM = false>
+// RM > 0 (with NR = 0) selects the rank-major vector tile of RM
+// kBlock-vector quarters (rank_major_any_tiles), folded one rank at a time by
+// fold_rank_major_any as in the flat rank-major body.
+template <class F, int OP, int NR, bool NT, int RM = 0>
 __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned char* table)
 {
     using Acc = typename F::Acc;
     constexpr int E = F::kEpv;
     const int n = NR > 0 ? NR : h.n;
-    // The tiles are split into S equal segments (S = rank count, like the
-    // flat kernel's chunk rows) and each segment gets every S-th workgroup,
-    // which strides through it: the workgroups in flight spread over the
-    // whole batch instead of one window of it, and every segment has the
-    // same work.
+    // A grid smaller than the tile count splits the tiles into S equal
+    // segments (S = rank count, like the flat kernel's chunk rows) and each
+    // segment gets every S-th workgroup, which strides through it: the
+    // workgroups in flight spread over the whole batch instead of one window
+    // of it, and every segment has the same work. A grid of one workgroup per
+    // tile takes the tiles in order (S = 1), as the flat rank-major kernels
+    // take their super tiles.
     const uint32_t G = gridDim.x;
-    const uint32_t S = min(static_cast<uint32_t>(h.n), G);
+    const uint32_t S = G >= h.ntiles ? 1u : min(static_cast<uint32_t>(h.n), G);
     const uint32_t seg = blockIdx.x % S;
     const uint32_t step = G / S + (seg < G % S ? 1u : 0u);
     const uint32_t L = (h.ntiles + S - 1) / S;
@@ -1228,15 +1229,6 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
     int pidx = multi_find_piece(pieces, h.npieces, t_first);
     MultiPiece pc = load_piece(pieces + pidx);
     uint32_t next0 = pidx + 1 < h.npieces ? pieces[pidx + 1].tile0 : UINT32_MAX;
-    // The rank-major tile keeps its piece's rank pointers (send in fold
-    // order, recv in rank order) across the piece's tiles instead of
-    // re-reading them from the table per tile, as the flat kernel holds its
-    // pointers for the whole grid-stride loop: 0.816 against 0.835 ms for
-    // 8 ranks x 256 MiB fp32 as 29 tensors.
-    constexpr int NRC = (RM && NR > 0) ? NR : 1;
-    const void* spc[NRC];
-    void* rpc[NRC];
-    int cached = -1;
     for (uint32_t tile = t_first; tile < t_end; tile += step) {
         if (tile >= next0) {
             do {
@@ -1260,8 +1252,8 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
             const uint64_t boff = a0 * (16 / E);
             uint64_t vb, ve;
             piece_vectors(pc.j0, j_end, a0, E, &vb, &ve);
-            if constexpr (RM && NR == 0) {
-                constexpr int M = rank_major_any_tiles(kRankMajorAnyMany, 16 / E);
+            if constexpr (RM > 0) {
+                constexpr int M = RM;
                 const uint64_t v = vb + static_cast<uint64_t>(ti) * (M * kBlock) + threadIdx.x;
                 if (ve > vb) {
                     // lanes past the piece read its first vector and drop it
@@ -1286,70 +1278,6 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
                         for (int m = 0; m < M; ++m)
                             if (ok[m]) stv_at<NT>(recv[r], off[m], out[m]);
                 }
-            } else if constexpr (RM && NR > 0) {
-                // the tile's four quarters: vectors v + m * kBlock of this
-                // thread; each stage loads them from one rank, the next
-                // rank's loads issued before the current rank's combine
-                constexpr int M = kMultiRankMajorTile / kBlock;
-                const uint64_t v = vb + static_cast<uint64_t>(ti) * kMultiRankMajorTile + threadIdx.x;
-                if (cached != pidx) {
-#pragma unroll
-                    for (int k = 0; k < NR; ++k) spc[k] = send[wrap_rank(c + k, NR)];
-#pragma unroll
-                    for (int k = 0; k < NR; ++k) rpc[k] = recv[k];
-                    cached = pidx;
-                }
-                const void* const* sp = spc;
-                uint64_t off[M];
-                bool ok[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    off[m] = (v + m * kBlock) * 16 + boff;
-                    ok[m] = v + m * kBlock < ve;
-                }
-                Acc acc[M][E];
-                u32x4 xc[M], xn[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (ok[m]) xc[m] = ldv_at<NT>(sp[0], off[m]);
-#pragma unroll
-                for (int k = 1; k <= NR; ++k) {
-                    if (k < NR) {
-#pragma unroll
-                        for (int m = 0; m < M; ++m)
-                            if (ok[m]) xn[m] = ldv_at<NT>(sp[k], off[m]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        if (ok[m]) {
-                            if (k == 1) {
-                                F::unpack(xc[m], acc[m]);
-                            } else {
-                                Acc t[E];
-                                F::unpack(xc[m], t);
-#pragma unroll
-                                for (int j = 0; j < E; ++j) acc[m][j] = combine<OP>(t[j], acc[m][j]);
-                            }
-                        }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (k < NR) {
-#pragma unroll
-                        for (int m = 0; m < M; ++m) xc[m] = xn[m];
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (ok[m]) {
-#pragma unroll
-                        for (int j = 0; j < E; ++j) acc[m][j] = finalize<OP>(acc[m][j], NR);
-                        xc[m] = F::pack(acc[m]);
-                    }
-#pragma unroll
-                for (int r = 0; r < NR; ++r)
-#pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        if (ok[m]) stv_at<NT>(rpc[r], off[m], xc[m]);
             } else {
                 // the tile's two halves: vectors v and v + kBlock of this thread
                 const uint64_t v = vb + static_cast<uint64_t>(ti) * kMultiVecTile + threadIdx.x;
@@ -1410,7 +1338,7 @@ __device__ __forceinline__ void multi_body(const MultiHeader& h, const unsigned 
     }
 }
 
-template <class F, int OP, int NR, bool NT, bool RM = false>
+template <class F, int OP, int NR, bool NT, int RM = 0>
 __global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
 {
     multi_body<F, OP, NR, NT, RM>(a.h, a.blob);
@@ -1601,11 +1529,15 @@ hipError_t multi_nr(const MultiArgs& a, bool rank_major, int grid_x, hipStream_t
 {
     const dim3 grid(grid_x), block(kBlock);
     if (rank_major) {
-        // the rank-major kernels: 8 ranks, or above 8, with non-temporal access
-        if (!NT || a.h.n < 8) return hipErrorInvalidValue;
+        // the rank-major kernel (run-time rank count, tiles of
+        // rank_major_any_tiles quarters), with non-temporal access from 4
+        // ranks
+        if (!NT || a.h.n < 4) return hipErrorInvalidValue;
         if constexpr (NT) {
-            if (a.h.n == 8) hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT, true>), grid, block, 0, s, a);
+            constexpr int MA = rank_major_any_tiles(kRankMajorAnyMany, 16 / F::kEpv);
+            constexpr int MF = rank_major_any_tiles(kRankMajorAnyMany - 1, 16 / F::kEpv);
+            if (a.h.n > 8) hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT, MA>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((multi_reduce<F, OP, 0, NT, MF>), grid, block, 0, s, a);
         }
     } else if (a.h.n == 8) {
         hipLaunchKernelGGL((multi_reduce<F, OP, 8, NT>), grid, block, 0, s, a);

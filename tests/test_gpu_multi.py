@@ -256,11 +256,12 @@ def test_bucket64_mixed_tensors_full_size(op):
 @pytest.mark.parametrize("dtype,op,shift", [("f32", "sum", 3), ("bf16", "avg", 0), ("f32", "max", 1),
                                             ("i32", "sum", 2)])
 def test_bucket8_rank_major_multi_full_compare(dtype, op, shift):
-    """8 ranks with more than 128 MiB of bucket per rank take the rank-major
-    multi-tensor kernel (four-quarter tiles). Views of log-uniform sizes into
-    one allocation per rank, its base shifted `shift` elements off a line:
-    every element against the oracle's fold over the flat bucket, and bit for
-    bit against the flat call."""
+    """8 ranks x 160 MiB of bucket: the streaming multi-tensor call takes the
+    rank-major kernel (tiles of four quarters, two for 16-bit types, one
+    workgroup per tile). Views of log-uniform sizes into one allocation per
+    rank, its base shifted `shift` elements off a line: every element against
+    the oracle's fold over the flat bucket, and bit for bit against the flat
+    call."""
     n = 8
     e = gu.ESIZE[dtype]
     count = (160 << 20) // e + 12_345
@@ -305,6 +306,43 @@ def test_bucket8_rank_major_multi_out_of_place():
         for b in row:
             assert b.guards_ok()
     del send, recv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n,dtype,op,shift,mib", [(4, "f32", "sum", 1, 40), (5, "f16", "avg", 3, 30),
+                                                  (6, "bf16", "max", 0, 24), (7, "i32", "prod", 2, 20),
+                                                  (8, "f16", "sum", 5, 18), (8, "f32", "min", 0, 17)])
+def test_rank_major_multi_few_ranks_full_compare(n, dtype, op, shift, mib):
+    """4 to 8 ranks with a footprint above half the last-level cache (the
+    default streams): the multi-tensor call takes the rank-major tiles for
+    run-time rank counts from 4 ranks, one workgroup per tile. Views of
+    log-uniform sizes into one allocation per rank, its base `shift`
+    elements off a line, in place: every element against the oracle's fold
+    over the flat bucket, and bit for bit against the flat call."""
+    e = gu.ESIZE[dtype]
+    count = (mib << 20) // e + 777
+    assert n * count * e > 128 << 20
+    sizes = synthetic.bucket_sizes(count, e, 4096, 16 << 20, seed=n + mib)
+    flat_in = gu.make_inputs(n, count, dtype, op, seed=n + 3 * shift)
+    bufs = [gu.RankBuf(count, dtype, offset=shift * e) for _ in range(n)]
+    for r in range(n):
+        bufs[r].view.copy_(flat_in[r])
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    rows = [[bufs[r].sub_ptr(int(o)) for r in range(n)] for o in offs]
+    flat = [x.clone() for x in flat_in]
+    with ar.Comm(n, 0) as comm:
+        ar.ar_all_reduce_multi(comm, rows, rows, sizes, dtype, op)
+        fp = [b.data_ptr() for b in flat]
+        ar.ar_all_reduce(comm, fp, fp, count, dtype, op, "fused")
+        torch.cuda.synchronize()
+    exp = gu.oracle_all_reduce(flat_in, dtype, op)
+    for r in range(n):
+        assert bufs[r].guards_ok(), f"rank {r} guard"
+        got = gu.host(bufs[r].view)
+        gu.assert_same(got, exp[r], dtype, f"rank-major multi n={n} {dtype} {op} rank {r} vs oracle")
+        gu.assert_same(got, gu.host(flat[r]), dtype, f"rank-major multi n={n} {dtype} {op} rank {r} vs flat")
+    print(f"{len(sizes)} tensors per rank")
+    del flat_in, bufs, flat
     torch.cuda.empty_cache()
 
 
