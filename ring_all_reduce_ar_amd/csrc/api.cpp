@@ -233,13 +233,14 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
 }
 
 // The rank-major all-reduce kernel (16-byte vectors, non-temporal access)
-// whenever the call streams, from 4 ranks. Measured against the kernels used
+// whenever the call streams, from 2 ranks. Measured against the kernels used
 // before on the same buffers (fp32 unless noted): at 8 ranks +15% cold at
 // 20-32 MiB per rank, +10% at 64 and 128 MiB, +5% at 256 MiB, +7.5% at
 // 1 GiB, +3.6% at 4 GiB, +3% at 14 GB fp16 (with one super tile per
 // workgroup, rank_major_grid); at 4 ranks +16% cold at 40 MiB and +6.6% at
+// 256 MiB; at 2 ranks +3% at 128 MiB, +10% at 1 GiB; at 3 ranks +16% at
 // 256 MiB; above 8 ranks see fused_rank_major_any.
-bool use_rank_major(int nranks, bool vec, bool nt) { return vec && nt && nranks >= 4; }
+bool use_rank_major(int nranks, bool vec, bool nt) { return vec && nt && nranks >= 2; }
 
 // Workgroups per chunk row for the rank-major all-reduce: one per super tile
 // (rank_major_any_tiles tiles of kBlock 16-byte vectors), so no workgroup
@@ -268,9 +269,18 @@ int rank_major_grid(uint64_t q, size_t elem, int nranks)
 int rank_major_scatter_grid(uint64_t q, size_t elem, int nranks)
 {
     const uint64_t tiles = ceil_div(ceil_div(q, 16 / elem), static_cast<uint64_t>(ar::kBlock));
-    const uint64_t m = nranks > 8 ? static_cast<uint64_t>(ar::rank_major_any_tiles(nranks, static_cast<int>(elem)))
-                                  : static_cast<uint64_t>(ar::kRankMajorTiles);
+    const uint64_t m = nranks >= 5 && nranks <= 8
+                           ? static_cast<uint64_t>(ar::kRankMajorTiles)
+                           : static_cast<uint64_t>(ar::rank_major_any_tiles(nranks, static_cast<int>(elem)));
     return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, m), 1, kMaxGridX));
+}
+
+// Workgroups per row for the tiled copies (all-gather, all-to-all): one per
+// tile of kRankMajorTiles x kBlock 16-byte vectors.
+int copy_tile_grid(uint64_t vectors)
+{
+    const uint64_t m = static_cast<uint64_t>(ar::kRankMajorTiles) * ar::kBlock;
+    return static_cast<int>(std::clamp<uint64_t>(ceil_div(vectors, m), 1, kMaxGridX));
 }
 
 // The multi-tensor call's rank-major tiles whenever the call streams, from 4
@@ -848,13 +858,16 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         a.q = q;
         a.n = n;
         const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, sbytes, rbytes), kLastLevelCacheBytes);
-        // Rank-major kernels beyond the last-level cache from 5 ranks up, one
-        // workgroup per super tile (+9 points at 256 MiB, +3.7 at 1 GiB, +1.5
-        // at 14 GB against the two-tile kernels on the same buffers with 8-16
-        // workgroups per CU; the exact grid then took 8 x 7e9 fp16 from 21.86
-        // to 20.85 ms and 8 x 64 MiB fp32 from 0.407 to 0.397 ms); above 8
-        // ranks the run-time rank-count body, as the all-reduce takes it.
-        const bool rank_major = vec && nt && n >= 5;
+        // Rank-major kernels beyond the last-level cache from 2 ranks, one
+        // workgroup per super tile: the fixed-rank-count body at 5..8 ranks
+        // (+9 points at 256 MiB, +3.7 at 1 GiB, +1.5 at 14 GB against the
+        // two-tile kernels on the same buffers with 8-16 workgroups per CU;
+        // the exact grid then took 8 x 7e9 fp16 from 21.86 to 20.85 ms and
+        // 8 x 64 MiB fp32 from 0.407 to 0.397 ms; the run-time body there
+        // measured 1-2% slower at 8 ranks, 1% faster at 5-6), the run-time
+        // one at 2..4 ranks (+8.7% at 4 x 64 MiB, +2.6% at 2 x 512 MiB of
+        // input against the two-tile kernel) and above 8.
+        const bool rank_major = vec && nt && n >= 2;
         const int gx_f = rank_major ? rank_major_scatter_grid(q, e, n)
                                     : grid_for(comm, vec ? ceil_div(q, epv) : q, n, n <= 2 ? 4 : 8);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
@@ -913,19 +926,24 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
     const int gx = grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n);
 
     if (!stepwise) {
-        // workgroups per CU: 4 for a single rank (a plain copy: 73.5% of
-        // peak at 1 GiB against 66.0% at 8), 3 at 2 ranks, 8 above
-        const int gx_f = grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n, n == 1 ? 4 : n == 2 ? 3 : 8);
         ar::CopyArgs a{};
         fill_ptrs(a, n, sendbufs, recvbufs);
         a.total = blk;
         a.n = n;
         const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, blk, rbytes), kLastLevelCacheBytes);
-        // Rank-major copy at 5..8 ranks from 512 MiB of input per rank
-        // (measured against the copy above at 8 ranks: +7.4 points at
-        // 512 MiB, +1.0 at 1 GiB, +6.6 at 1.75 GB; 1-4 points slower at
-        // 64-256 MiB).
-        const bool rank_major = vec && nt && n >= 5 && n <= 8 && blk >= (size_t(512) << 20);
+        // Streaming: the rank-major copy (kRankMajorTiles vectors per thread
+        // loaded once, stored to every rank), one workgroup per tile; against
+        // the grid-stride copies used before on the same buffers, fp32: 1 rank
+        // x 1 GiB (a plain copy) 0.357 -> 0.341 ms, 8 x 32 MiB in 0.435 ->
+        // 0.363 ms, 8 x 128 MiB 1.71 -> 1.48 ms, 2 x 512 MiB 0.597 -> 0.558 ms,
+        // 8 x 1.75 GB fp16 22.06 -> 21.93 ms, 16 x 8 MiB level. Cached: one
+        // vector per thread per step, 4 workgroups per CU for a single rank
+        // (a plain copy: 73.5% of peak at 1 GiB against 66.0% at 8), 3 at 2
+        // ranks, 8 above.
+        const bool rank_major = vec && nt;
+        const int gx_f = rank_major ? copy_tile_grid(blk / 16)
+                                    : grid_for(comm, vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n,
+                                               n == 1 ? 4 : n == 2 ? 3 : 8);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_fused_gather(a, vec, nt, rank_major, gx_f, s);
             return err != hipSuccess ? err : tick(t);
@@ -1001,12 +1019,17 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
     const bool nt = use_nt(2 * static_cast<uint64_t>(n) * total);
     if (!stepwise) {
         a.step = -1;
-        // 4 workgroups per CU: each moves one block pair, a plain copy stream
-        // (8 ranks x 256 MiB: 69.3% against 62.2% at 8)
-        const int gx = grid_for(comm, units, n * n, 4);
+        // Streaming: the tiled copy, one workgroup per tile, so block pairs
+        // are copied one after another (against 4 workgroups per CU on the
+        // same buffers, fp32: 8 x 256 MiB 0.776 -> 0.711 ms, 8 x 32 MiB 93.4
+        // -> 88.0 us, 4 x 512 MiB 0.774 -> 0.720 ms, 16 x 64 MiB 0.387 ->
+        // 0.392 ms). Cached: 4 workgroups per CU, each moving one block pair
+        // (8 ranks x 256 MiB: 69.3% against 62.2% at 8).
         const bool nt1 = call_nt(comm, 2 * static_cast<uint64_t>(n) * total, kLastLevelCacheBytes);
+        const bool tiled = vec && nt1;
+        const int gx = tiled ? copy_tile_grid(blk / 16) : grid_for(comm, units, n * n, 4);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_all_to_all(a, vec, nt1, gx, s);
+            hipError_t err = ar::launch_all_to_all(a, vec, nt1, tiled, gx, s);
             return err != hipSuccess ? err : tick(t);
         });
     }
@@ -1014,7 +1037,7 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int st = 0; st < n; ++st) {
             a.step = st;
-            hipError_t err = ar::launch_all_to_all(a, vec, nt, gx, s);
+            hipError_t err = ar::launch_all_to_all(a, vec, nt, false, gx, s);
             if (err == hipSuccess) err = tick(t);
             if (err != hipSuccess) return err;
         }

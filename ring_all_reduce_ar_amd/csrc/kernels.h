@@ -119,7 +119,8 @@ constexpr int kMultiBlobBytes = 3840;
 constexpr int kMultiVecTile = 2 * kBlock;
 
 // Tiles a thread of the fixed-rank-count rank-major kernels (reduce-scatter at
-// 5..8 ranks, the rank-major all-gather copy) takes together.
+// 5..8 ranks) and of the tiled copies (all-gather, all-to-all) takes
+// together.
 constexpr int kRankMajorTiles = 4;
 
 // Tiles (of kBlock 16-byte vectors) per super tile of the rank-major kernels
@@ -163,14 +164,15 @@ struct A2AArgs {
     int step;
 };
 
-hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream);
+// `tiled` selects the tiled copy (needs vec and nt): kRankMajorTiles vectors
+// per thread and step, best with one workgroup per tile.
+hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, bool tiled, int grid_x, hipStream_t stream);
 
 // Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
 // has checked that every rank pointer is 16-byte aligned, and for the
 // reduce-scatter layout also q % (16/elem) == 0); `nt` selects non-temporal
 // loads and stores (footprints beyond the last-level cache) over cached ones;
-// `rank_major` selects the rank-major kernels (needs vec and nt; the
-// reduce-scatter layout also 5 ranks or more). Any grid is correct (the
+// `rank_major` selects the rank-major kernels (needs vec and nt). Any grid is correct (the
 // kernels stride by it); the rank-major ones run best with one workgroup per
 // super tile.
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,

@@ -115,9 +115,14 @@ hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, int grid_x, hipStream_t stream)
+hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, bool tiled, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.step < 0 ? a.n * a.n : a.n);
+    if (tiled) {
+        if (!vec || !nt) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((a2a_copy<true, true, true>), grid, dim3(kBlock), 0, stream, a);
+        return hipGetLastError();
+    }
     if (!vec) hipLaunchKernelGGL((a2a_copy<false, true>), grid, dim3(kBlock), 0, stream, a);
     else if (nt) hipLaunchKernelGGL((a2a_copy<true, true>), grid, dim3(kBlock), 0, stream, a);
     else hipLaunchKernelGGL((a2a_copy<true, false>), grid, dim3(kBlock), 0, stream, a);

@@ -738,7 +738,7 @@ __global__ __launch_bounds__(kBlock) void fused_gather(const CopyArgs a)
             for (int m = 0; m < M; ++m) {
                 vv[m] = (st * M + m) * kBlock + threadIdx.x;
                 ok[m] = vv[m] < nv;
-                if (ok[m]) x[m] = ldv<NT>(a.send[p], vv[m]);
+                x[m] = ldv<NT>(a.send[p], ok[m] ? vv[m] : 0);  // lanes past the block reload vector 0
             }
             for (int r = 0; r < a.n; ++r)
 #pragma unroll
@@ -1348,7 +1348,11 @@ __global__ __launch_bounds__(kBlock) void multi_reduce(const MultiArgs a)
 // all-to-all [handbook "集合通信原语", section 五个原语]: rank r's block p
 // becomes rank p's block r
 // ---------------------------------------------------------------------------
-template <bool VEC, bool NT>
+// TILED (16-byte vectors, non-temporal): a thread copies kRankMajorTiles
+// vectors a kBlock apart per step, all loads before the stores, and the host
+// launches one workgroup per such tile, so the resident workgroups stream
+// one block pair after another.
+template <bool VEC, bool NT, bool TILED = false>
 __global__ __launch_bounds__(kBlock) void a2a_copy(const A2AArgs a)
 {
     const int y = blockIdx.y;
@@ -1364,7 +1368,24 @@ __global__ __launch_bounds__(kBlock) void a2a_copy(const A2AArgs a)
     char* dst = static_cast<char*>(a.recv[p]) + static_cast<uint64_t>(r) * a.blk;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     const uint64_t t0 = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if constexpr (VEC) {
+    if constexpr (TILED) {
+        static_assert(VEC, "the tiled copy takes 16-byte vectors");
+        constexpr int M = kRankMajorTiles;
+        const uint64_t nv = a.blk / 16;
+        const uint64_t ntiles = (nv + M * kBlock - 1) / (M * kBlock);
+        for (uint64_t st = blockIdx.x; st < ntiles; st += gridDim.x) {
+            u32x4 x[M];
+            uint64_t vv[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                vv[m] = (st * M + m) * kBlock + threadIdx.x;
+                x[m] = ldv<NT>(src, vv[m] < nv ? vv[m] : 0);  // lanes past the block reload vector 0
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                if (vv[m] < nv) stv<NT>(dst, vv[m], x[m]);
+        }
+    } else if constexpr (VEC) {
         const uint64_t nv = a.blk / 16;
         for (uint64_t v = t0; v < nv; v += stride) stv<NT>(dst, v, ldv<NT>(src, v));
     } else {

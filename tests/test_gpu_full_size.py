@@ -202,6 +202,27 @@ def test_grad7b_reduce_scatter_then_all_gather():
     free()
 
 
+@pytest.mark.parametrize("n,dtype,blk", [(2, "f32", 20_000_004), (4, "f16", 9_000_008), (16, "bf16", 600_008),
+                                         (5, "f32", 3_000_004)])
+def test_all_to_all_tiled_full_compare(n, dtype, blk):
+    """Beyond the last-level cache the fused all-to-all takes the tiled copy
+    (four vectors per thread, one workgroup per tile, ragged last tiles):
+    every element of every rank against the oracle's transpose."""
+    assert 2 * n * n * blk * gu.ESIZE[dtype] > 256 << 20
+    xs = gu.make_inputs(n, n * blk, dtype, "sum", seed=n + blk % 97)
+    exp = oracle.all_to_all([gu.host(x) for x in xs], dtype)
+    with ar.Comm(n, 0) as comm:
+        recv = [gu.RankBuf(n * blk, dtype) for _ in range(n)]
+        ar.ar_all_to_all(comm, [x.data_ptr() for x in xs], [b.ptr() for b in recv], blk, dtype, "fused")
+        torch.cuda.synchronize()
+        for p in range(n):
+            assert recv[p].guards_ok(), f"rank {p} guard"
+            gu.assert_same(gu.host(recv[p].view), exp[p], dtype, f"all-to-all n={n} {dtype} blk={blk} rank {p}")
+        del recv
+    del xs, exp
+    free()
+
+
 def test_all_to_all_256mib_fp32_full_compare():
     """All-to-all of 8 x 256 MiB fp32 (the `--collective all_to_all` sweep
     point), every element against the oracle's transpose."""
@@ -340,6 +361,28 @@ def test_rank_major_from_64mib_full_compare(n, dtype, op, count):
     free()
 
 
+@pytest.mark.parametrize("n,dtype,op,count,inplace", [
+    (2, "f32", "sum", 22_368_261, False),
+    (3, "f32", "max", 33_554_435, True),
+    (2, "bf16", "avg", 50_000_003, True),
+    (3, "f16", "prod", 30_000_001, False),
+])
+def test_rank_major_two_three_ranks_full_compare(n, dtype, op, count, inplace):
+    """2 and 3 ranks with a footprint above half the last-level cache: the
+    all-reduce streams through its rank-major kernel (one workgroup per super
+    tile) at these rank counts too. Every element of every rank against the
+    oracle, ragged chunks, guard bands."""
+    assert n * count * gu.ESIZE[dtype] > 128 << 20
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=count % 1009)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "fused", inplace=inplace)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} inplace={inplace} rank {r}")
+        del xs, exp, got, send, recv
+    free()
+
+
 @pytest.mark.parametrize("n,count,dtype", [(8, 1 << 30, "f32"), (8, (1 << 31) - 5, "f16"), (6, 999_999_997, "f32")])
 def test_rank_major_upper_sizes_sampled(n, count, dtype):
     """The rank-major all-reduce at 2.4-4 GiB per rank, in place as the
@@ -354,6 +397,9 @@ def test_rank_major_upper_sizes_sampled(n, count, dtype):
 
 
 @pytest.mark.parametrize("n,dtype,op,rc,inplace", [
+    (2, "f32", "sum", 20_000_004, True),
+    (3, "bf16", "avg", 12_000_000, False),
+    (4, "f16", "max", 9_000_008, False),
     (8, "f32", "sum", 4_500_004, False),
     (5, "f16", "avg", 14_000_008, True),
     (7, "bf16", "max", 9_999_992, False),
@@ -363,8 +409,8 @@ def test_rank_major_upper_sizes_sampled(n, count, dtype):
     (12, "i32", "max", 3_000_000, False),
 ])
 def test_reduce_scatter_rank_major_full_compare(n, dtype, op, rc, inplace):
-    """Reduce-scatter from 5 ranks beyond the last-level cache takes the
-    rank-major kernels (fixed rank count up to 8, run-time above; block
+    """Reduce-scatter from 2 ranks beyond the last-level cache takes the
+    rank-major kernels (fixed rank count at 5-8, run-time otherwise; block
     lengths here are whole 16-byte vectors, as the vector kernels need):
     every element of every rank's block against the oracle's reduce-scatter,
     out of place or in place (recv[r] inside send[r] at block r), with guard
@@ -393,10 +439,13 @@ def test_reduce_scatter_rank_major_full_compare(n, dtype, op, rc, inplace):
     free()
 
 
-@pytest.mark.parametrize("n,dtype,sc,inplace", [(5, "f32", 134_217_732, False), (8, "f16", 268_435_464, True)])
+@pytest.mark.parametrize("n,dtype,sc,inplace", [(5, "f32", 134_217_732, False), (8, "f16", 268_435_464, True),
+                                               (1, "f32", 40_000_004, False), (2, "f16", 40_000_008, True),
+                                               (3, "bf16", 16_000_000, False), (16, "f32", 1_048_580, False)])
 def test_all_gather_rank_major_full_compare(n, dtype, sc, inplace):
-    """From 512 MiB of input per rank at 5-8 ranks the all-gather takes its
-    rank-major copy (four consecutive tiles per thread, stored rank by rank).
+    """Beyond the last-level cache the all-gather takes its rank-major copy
+    (four consecutive tiles per thread, stored rank by rank, one workgroup
+    per tile) at every rank count, one rank (a plain copy) included.
     All-gather is concatenation in rank order (handbook "集合通信原语",
     section 五个原语), so every output block of every rank is compared bit
     for bit with its input block on the device; the tails are ragged and the
