@@ -242,8 +242,23 @@ uint64_t footprint(int n, const void* const send[], void* const recv[], uint64_t
 // 256 MiB; above 8 ranks see fused_rank_major_any.
 bool use_rank_major(int nranks, bool vec, bool nt) { return vec && nt && nranks >= 2; }
 
+// Tiles per super tile of the rank-major all-reduce: rank_major_any_tiles,
+// or one for 16-bit types at up to 8 ranks from kOneTileBytes per rank.
+int allreduce_tiles(int nranks, size_t elem, size_t bytes_per_rank)
+{
+    if (elem == 2 && nranks <= 8 && bytes_per_rank >= ar::kOneTileBytes) return 1;
+    return ar::rank_major_any_tiles(nranks, static_cast<int>(elem));
+}
+
+// The same for the reduce-scatter layout: kScatterTiles for the
+// fixed-rank-count body at 5..8 ranks, else rank_major_any_tiles.
+int scatter_tiles(int nranks, size_t elem)
+{
+    return nranks >= 5 && nranks <= 8 ? ar::kScatterTiles : ar::rank_major_any_tiles(nranks, static_cast<int>(elem));
+}
+
 // Workgroups per chunk row for the rank-major all-reduce: one per super tile
-// (rank_major_any_tiles tiles of kBlock 16-byte vectors), so no workgroup
+// (`m` tiles of kBlock 16-byte vectors), so no workgroup
 // strides through its row. The hardware dispatches workgroups in order, so
 // the resident ones work through one chunk row after another, each on its
 // own contiguous super tile. Against a grid-stride grid of 16 workgroups
@@ -255,24 +270,18 @@ bool use_rank_major(int nranks, bool vec, bool nt) { return vec && nt && nranks 
 // more than kMaxGridX super tiles (chunks beyond 64 GiB) stays correct.
 constexpr uint64_t kMaxGridX = (uint64_t(1) << 32) / ar::kBlock - 1;  // work-items per dimension fit 32 bits
 
-int rank_major_grid(uint64_t q, size_t elem, int nranks)
+int rank_major_grid(uint64_t q, size_t elem, int m)
 {
     const uint64_t tiles = ceil_div(ceil_div(q, 16 / elem), static_cast<uint64_t>(ar::kBlock)) + 1;
-    const uint64_t m = static_cast<uint64_t>(ar::rank_major_any_tiles(nranks, static_cast<int>(elem)));
-    return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, m), 1, kMaxGridX));
+    return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, static_cast<uint64_t>(m)), 1, kMaxGridX));
 }
 
 // The same for the reduce-scatter layout, whose tiles count from the chunk
-// start (block c of the output): the fixed-rank-count body at 5..8 ranks
-// takes kRankMajorTiles tiles per super tile, the run-time one
-// rank_major_any_tiles.
-int rank_major_scatter_grid(uint64_t q, size_t elem, int nranks)
+// start (block c of the output).
+int rank_major_scatter_grid(uint64_t q, size_t elem, int m)
 {
     const uint64_t tiles = ceil_div(ceil_div(q, 16 / elem), static_cast<uint64_t>(ar::kBlock));
-    const uint64_t m = nranks >= 5 && nranks <= 8
-                           ? static_cast<uint64_t>(ar::kRankMajorTiles)
-                           : static_cast<uint64_t>(ar::rank_major_any_tiles(nranks, static_cast<int>(elem)));
-    return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, m), 1, kMaxGridX));
+    return static_cast<int>(std::clamp<uint64_t>(ceil_div(tiles, static_cast<uint64_t>(m)), 1, kMaxGridX));
 }
 
 // Workgroups per row for the tiled copies (all-gather, all-to-all): one per
@@ -739,11 +748,11 @@ ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* 
         a.q = q;
         a.n = n;
         const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, bytes, bytes), kAllReduceStreamBytes);
-        const bool rank_major = use_rank_major(n, vec, nt);
-        const int gx = rank_major ? rank_major_grid(q, e, n)
+        const int rm_tiles = use_rank_major(n, vec, nt) ? allreduce_tiles(n, e, bytes) : 0;
+        const int gx = rm_tiles ? rank_major_grid(q, e, rm_tiles)
                                   : grid_for(comm, vec ? ceil_div(q, epv) : q, n, fused_per_cu(bytes, n, !nt));
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rank_major, gx, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, false, vec, nt, rm_tiles, gx, s);
             return err != hipSuccess ? err : tick(t);
         }, timing);
     }
@@ -864,14 +873,17 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
         // two-tile kernels on the same buffers with 8-16 workgroups per CU;
         // the exact grid then took 8 x 7e9 fp16 from 21.86 to 20.85 ms and
         // 8 x 64 MiB fp32 from 0.407 to 0.397 ms; the run-time body there
-        // measured 1-2% slower at 8 ranks, 1% faster at 5-6), the run-time
-        // one at 2..4 ranks (+8.7% at 4 x 64 MiB, +2.6% at 2 x 512 MiB of
-        // input against the two-tile kernel) and above 8.
+        // measured 1-2% slower at 8 ranks, 1% faster at 5-6; one tile per
+        // super tile there against four: 8 x 7e9 fp16 20.65 -> 20.17 ms,
+        // 8 x 256 MiB fp32 0.411 -> 0.401 ms), the run-time one at 2..4 ranks
+        // (+8.7% at 4 x 64 MiB, +2.6% at 2 x 512 MiB of input against the
+        // two-tile kernel) and above 8.
         const bool rank_major = vec && nt && n >= 2;
-        const int gx_f = rank_major ? rank_major_scatter_grid(q, e, n)
+        const int rm_tiles = rank_major ? scatter_tiles(n, e) : 0;
+        const int gx_f = rank_major ? rank_major_scatter_grid(q, e, rm_tiles)
                                     : grid_for(comm, vec ? ceil_div(q, epv) : q, n, n <= 2 ? 4 : 8);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
-            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, rank_major, gx_f, s);
+            hipError_t err = ar::launch_fused_reduce(a, dtype, op, true, vec, nt, rm_tiles, gx_f, s);
             return err != hipSuccess ? err : tick(t);
         });
     }

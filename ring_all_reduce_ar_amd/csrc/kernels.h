@@ -118,10 +118,11 @@ constexpr int kMultiBlobBytes = 3840;
 // kernel; element pieces into tiles of kBlock elements.
 constexpr int kMultiVecTile = 2 * kBlock;
 
-// Tiles a thread of the fixed-rank-count rank-major kernels (reduce-scatter at
-// 5..8 ranks) and of the tiled copies (all-gather, all-to-all) takes
-// together.
+// Tiles a thread of the tiled copies (all-gather, all-to-all) takes together.
 constexpr int kRankMajorTiles = 4;
+// Tiles per super tile of the fixed-rank-count rank-major reduce-scatter
+// (5..8 ranks).
+constexpr int kScatterTiles = 1;
 
 // Tiles (of kBlock 16-byte vectors) per super tile of the rank-major kernels
 // for run-time rank counts: 8 above 8 ranks and 4 up to 8 for 4-byte types
@@ -168,15 +169,25 @@ struct A2AArgs {
 // per thread and step, best with one workgroup per tile.
 hipError_t launch_all_to_all(const A2AArgs& a, bool vec, bool nt, bool tiled, int grid_x, hipStream_t stream);
 
+// A super tile of one tile for 16-bit types at up to 8 ranks from this many
+// bytes per rank, instead of rank_major_any_tiles. Against two tiles on the
+// same buffers, fp16 at 8 ranks: +4.4% at 14 GB, +2.5% at 1 GiB, +1.5% at
+// 4 GiB, -1.2% at 256 MiB, -4.3% at 64 MiB; the benchmark's first allocation
+// of 8 x 14 GB: 38.0 -> 35.9 ms.
+constexpr uint64_t kOneTileBytes = uint64_t(1) << 30;
+
 // Fused single-pass reduction; `vec` selects the 16-byte kernels (the caller
 // has checked that every rank pointer is 16-byte aligned, and for the
 // reduce-scatter layout also q % (16/elem) == 0); `nt` selects non-temporal
 // loads and stores (footprints beyond the last-level cache) over cached ones;
-// `rank_major` selects the rank-major kernels (needs vec and nt). Any grid is correct (the
+// `rank_major_tiles` > 0 selects the rank-major kernels (needs vec and nt)
+// with that many tiles per super tile: kScatterTiles for the reduce-scatter
+// layout at 5..8 ranks, else rank_major_any_tiles, or 1 for a 16-bit
+// all-reduce at up to 8 ranks (other values are rejected). Any grid is correct (the
 // kernels stride by it); the rank-major ones run best with one workgroup per
 // super tile.
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
-                               bool rank_major, int grid_x, hipStream_t stream);
+                               int rank_major_tiles, int grid_x, hipStream_t stream);
 
 // Fused all-gather: block p of send[p] (blk bytes) to recv[r] + p*blk for all r.
 // `rank_major` selects the rank-major copy (needs vec and nt).

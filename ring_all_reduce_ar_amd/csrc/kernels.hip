@@ -8,14 +8,14 @@ using namespace detail;
 
 namespace {
 template <bool SC>
-hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, bool rank_major,
+hipError_t fused_dtype(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, bool nt, int rank_major_tiles,
                        dim3 grid, hipStream_t s)
 {
     switch (dtype) {
-    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, nt, rank_major, grid, s);
-    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, nt, rank_major, grid, s);
-    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, nt, rank_major, grid, s);
-    case AR_INT32: return fused_op<I32, SC>(a, op, vec, nt, rank_major, grid, s);
+    case AR_FLOAT32: return fused_op<F32, SC>(a, op, vec, nt, rank_major_tiles, grid, s);
+    case AR_FLOAT16: return fused_op<F16, SC>(a, op, vec, nt, rank_major_tiles, grid, s);
+    case AR_BFLOAT16: return fused_op<BF16, SC>(a, op, vec, nt, rank_major_tiles, grid, s);
+    case AR_INT32: return fused_op<I32, SC>(a, op, vec, nt, rank_major_tiles, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -74,11 +74,11 @@ hipError_t launch_multi_reduce(const MultiArgs& a, ar_dtype_t dtype, ar_op_t op,
 }
 
 hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op, bool scatter, bool vec, bool nt,
-                               bool rank_major, int grid_x, hipStream_t stream)
+                               int rank_major_tiles, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
-    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, rank_major, grid, stream)
-                   : fused_dtype<false>(a, dtype, op, vec, nt, rank_major, grid, stream);
+    return scatter ? fused_dtype<true>(a, dtype, op, vec, nt, rank_major_tiles, grid, stream)
+                   : fused_dtype<false>(a, dtype, op, vec, nt, rank_major_tiles, grid, stream);
 }
 
 hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, bool rank_major, int grid_x, hipStream_t stream)

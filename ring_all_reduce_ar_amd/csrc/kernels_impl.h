@@ -1420,36 +1420,49 @@ hipError_t fused_nr(const ReduceArgs& a, dim3 grid, hipStream_t s)
 // and 2-7% faster at 20-64 MiB); the reduce-scatter layout takes the
 // fixed-rank-count body at 5..8 ranks, the run-time one above.
 template <class F, int OP, bool SC>
-hipError_t fused_nr_rank_major(const ReduceArgs& a, dim3 grid, hipStream_t s)
+hipError_t fused_nr_rank_major(const ReduceArgs& a, int tiles, dim3 grid, hipStream_t s)
 {
     const dim3 block(kBlock);
-    constexpr int M = kRankMajorTiles;
+    constexpr int M = kScatterTiles;
     constexpr int MA = rank_major_any_tiles(kRankMajorAnyMany, 16 / F::kEpv);
     constexpr int MF = rank_major_any_tiles(kRankMajorAnyMany - 1, 16 / F::kEpv);
     if (a.n > 8) {
+        if (tiles != MA) return hipErrorInvalidValue;
         hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MA>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if constexpr (SC) {
-        switch (a.n) {
-        case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, M>), grid, block, 0, s, a); break;
-        case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, M>), grid, block, 0, s, a); break;
-        case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, M>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, M>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MF>), grid, block, 0, s, a); break;
+        if (a.n >= 5) {
+            if (tiles != M) return hipErrorInvalidValue;
+            switch (a.n) {
+            case 5: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 5, SC, true, M>), grid, block, 0, s, a); break;
+            case 6: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 6, SC, true, M>), grid, block, 0, s, a); break;
+            case 7: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 7, SC, true, M>), grid, block, 0, s, a); break;
+            default: hipLaunchKernelGGL((fused_reduce_vec<F, OP, 8, SC, true, M>), grid, block, 0, s, a); break;
+            }
+            return hipGetLastError();
         }
-    } else {
-        hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MF>), grid, block, 0, s, a);
     }
-    return hipGetLastError();
+    if (tiles == MF) {
+        hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, MF>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    if constexpr (F::kEpv == 8 && !SC) {
+        // 16-bit all-reduce, one tile per super tile (large buffers)
+        if (tiles == 1) {
+            hipLaunchKernelGGL((fused_reduce_vec<F, OP, 0, SC, true, 1>), grid, block, 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <class F, int OP, bool SC>
-hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, bool rank_major, dim3 grid, hipStream_t s)
+hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, int rank_major_tiles, dim3 grid, hipStream_t s)
 {
-    if (rank_major) {
+    if (rank_major_tiles > 0) {
         if (!vec || !nt) return hipErrorInvalidValue;
-        return fused_nr_rank_major<F, OP, SC>(a, grid, s);
+        return fused_nr_rank_major<F, OP, SC>(a, rank_major_tiles, grid, s);
     }
     if (!vec) {
         hipLaunchKernelGGL((fused_reduce_scalar<F, OP, SC>), grid, dim3(kBlock), 0, s, a);
@@ -1459,14 +1472,15 @@ hipError_t fused_n(const ReduceArgs& a, bool vec, bool nt, bool rank_major, dim3
 }
 
 template <class F, bool SC>
-hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, bool nt, bool rank_major, dim3 grid, hipStream_t s)
+hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, bool nt, int rank_major_tiles, dim3 grid,
+                    hipStream_t s)
 {
     switch (op) {
-    case AR_SUM: return fused_n<F, AR_SUM, SC>(a, vec, nt, rank_major, grid, s);
-    case AR_AVG: return fused_n<F, AR_AVG, SC>(a, vec, nt, rank_major, grid, s);
-    case AR_MAX: return fused_n<F, AR_MAX, SC>(a, vec, nt, rank_major, grid, s);
-    case AR_MIN: return fused_n<F, AR_MIN, SC>(a, vec, nt, rank_major, grid, s);
-    case AR_PROD: return fused_n<F, AR_PROD, SC>(a, vec, nt, rank_major, grid, s);
+    case AR_SUM: return fused_n<F, AR_SUM, SC>(a, vec, nt, rank_major_tiles, grid, s);
+    case AR_AVG: return fused_n<F, AR_AVG, SC>(a, vec, nt, rank_major_tiles, grid, s);
+    case AR_MAX: return fused_n<F, AR_MAX, SC>(a, vec, nt, rank_major_tiles, grid, s);
+    case AR_MIN: return fused_n<F, AR_MIN, SC>(a, vec, nt, rank_major_tiles, grid, s);
+    case AR_PROD: return fused_n<F, AR_PROD, SC>(a, vec, nt, rank_major_tiles, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1591,8 +1605,8 @@ hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, bool rank_major, in
 // stepwise reduce-scatter, multi-tensor) in dtype_<name>.hip and the tree
 // kernels in tree_<name>.hip, so the build compiles them in parallel.
 #define AR_RING_INSTANTIATIONS(F, EXTERN)                                                                       \
-    EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, bool, dim3, hipStream_t); \
-    EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, bool, dim3, hipStream_t); \
+    EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, int, dim3, hipStream_t);  \
+    EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, int, dim3, hipStream_t); \
     EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, dim3, hipStream_t);                       \
     EXTERN template hipError_t multi_op<F>(const MultiArgs&, ar_op_t, bool, bool, int, hipStream_t);
 #define AR_TREE_INSTANTIATIONS(F, EXTERN)                                                           \

@@ -383,6 +383,22 @@ def test_rank_major_two_three_ranks_full_compare(n, dtype, op, count, inplace):
     free()
 
 
+@pytest.mark.parametrize("n,dtype,op,count,inplace", [(2, "f16", "sum", (1 << 29) + 5, True),
+                                                    (3, "bf16", "max", (1 << 29) + 11, False)])
+def test_one_tile_super_tiles_full_compare(n, dtype, op, count, inplace):
+    """16-bit all-reduces of 1 GiB per rank and more at up to 8 ranks take
+    super tiles of one tile: every element of every rank against the oracle,
+    ragged chunks, guard bands."""
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=n + 31)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "fused", inplace=inplace)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"n={n} {dtype} {op} count={count} inplace={inplace} rank {r}")
+        del xs, exp, got, send, recv
+    free()
+
+
 @pytest.mark.parametrize("n,count,dtype", [(8, 1 << 30, "f32"), (8, (1 << 31) - 5, "f16"), (6, 999_999_997, "f32")])
 def test_rank_major_upper_sizes_sampled(n, count, dtype):
     """The rank-major all-reduce at 2.4-4 GiB per rank, in place as the
