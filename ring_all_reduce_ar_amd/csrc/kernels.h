@@ -193,9 +193,16 @@ hipError_t launch_fused_reduce(const ReduceArgs& a, ar_dtype_t dtype, ar_op_t op
 // `rank_major` selects the rank-major copy (needs vec and nt).
 hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, bool rank_major, int grid_x, hipStream_t stream);
 
-hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x, hipStream_t stream);
+// Vectors a thread takes per tile in the tiled ring steps.
+constexpr int kStepTiles = 4;
 
-hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);
+// One ring step. `tiles` = 0: one vector (or element) per thread per
+// grid-stride step; `tiles` = kStepTiles (needs vec): the tiled form, best
+// with one workgroup per tile; `nt` selects non-temporal access for it.
+hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int tiles, bool nt, int grid_x,
+                          hipStream_t stream);
+
+hipError_t launch_copy_step(const CopyArgs& a, bool vec, int tiles, bool nt, int grid_x, hipStream_t stream);
 
 // send[r] -> recv[r] + r*dst_stride, total bytes, for every rank.
 hipError_t launch_local_copy(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream);

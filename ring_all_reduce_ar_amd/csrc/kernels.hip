@@ -95,23 +95,31 @@ hipError_t launch_fused_gather(const CopyArgs& a, bool vec, bool nt, bool rank_m
     return hipGetLastError();
 }
 
-hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int grid_x, hipStream_t stream)
+hipError_t launch_rs_step(const StepArgs& a, ar_dtype_t dtype, ar_op_t op, bool vec, int tiles, bool nt, int grid_x,
+                          hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
     switch (dtype) {
-    case AR_FLOAT32: return rs_op<F32>(a, op, vec, grid, stream);
-    case AR_FLOAT16: return rs_op<F16>(a, op, vec, grid, stream);
-    case AR_BFLOAT16: return rs_op<BF16>(a, op, vec, grid, stream);
-    case AR_INT32: return rs_op<I32>(a, op, vec, grid, stream);
+    case AR_FLOAT32: return rs_op<F32>(a, op, vec, tiles, nt, grid, stream);
+    case AR_FLOAT16: return rs_op<F16>(a, op, vec, tiles, nt, grid, stream);
+    case AR_BFLOAT16: return rs_op<BF16>(a, op, vec, tiles, nt, grid, stream);
+    case AR_INT32: return rs_op<I32>(a, op, vec, tiles, nt, grid, stream);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_copy_step(const CopyArgs& a, bool vec, int grid_x, hipStream_t stream)
+hipError_t launch_copy_step(const CopyArgs& a, bool vec, int tiles, bool nt, int grid_x, hipStream_t stream)
 {
     const dim3 grid(grid_x, a.n);
-    if (vec) hipLaunchKernelGGL((copy_step<true>), grid, dim3(kBlock), 0, stream, a);
-    else hipLaunchKernelGGL((copy_step<false>), grid, dim3(kBlock), 0, stream, a);
+    if (tiles > 0) {
+        if (!vec || tiles != kStepTiles) return hipErrorInvalidValue;
+        if (nt) hipLaunchKernelGGL((copy_step<true, true, kStepTiles>), grid, dim3(kBlock), 0, stream, a);
+        else hipLaunchKernelGGL((copy_step<true, false, kStepTiles>), grid, dim3(kBlock), 0, stream, a);
+    } else if (vec) {
+        hipLaunchKernelGGL((copy_step<true>), grid, dim3(kBlock), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((copy_step<false>), grid, dim3(kBlock), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

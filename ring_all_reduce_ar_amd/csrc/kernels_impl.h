@@ -826,7 +826,82 @@ __device__ __forceinline__ void rs_elem(const StepArgs& a, int r, int left, int 
 // writes (rank r, chunk c) and reads from the left (rank r-1, chunk c) are
 // disjoint from what rank r-1 writes in the same step (its chunk c-1), so no
 // staging buffer is needed.
-template <class F, int OP, bool VEC>
+// The tiled form of a reduce-scatter step's whole vectors: a thread takes M
+// vectors a kBlock apart per tile, issues all their loads (local, incoming)
+// before combining, and the host launches one workgroup per tile, so the
+// resident workgroups move through each rank's chunk in order.
+template <class F, int OP, bool NT, int M>
+__device__ __forceinline__ void rs_step_tiles(const StepArgs& a, int r, int left, int c, uint64_t v0, uint64_t nv)
+{
+    using Acc = typename F::Acc;
+    constexpr int E = F::kEpv;
+    constexpr int W = E / 4;  // 16-byte workspace vectors per element vector (fp32 partials)
+    const int n = a.n;
+    const uint64_t ntiles = (nv + M * kBlock - 1) / (M * kBlock);
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        uint64_t vi[M];
+        bool ok[M];
+        u32x4 xl[M], xi[M][W];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const uint64_t v = (t * M + m) * kBlock + threadIdx.x;
+            ok[m] = v < nv;
+            vi[m] = v0 + (ok[m] ? v : 0);  // lanes past the chunk reload its first vector
+            xl[m] = ldv<NT>(a.send[r], vi[m]);
+        }
+        const bool from_ws = !a.first && a.ws;
+        if (a.first) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) xi[m][0] = ldv<NT>(a.send[left], vi[m]);
+        } else if (from_ws) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int j = 0; j < W; ++j) xi[m][j] = ldv<NT>(a.ws, vi[m] * W + j);
+        } else {
+#pragma unroll
+            for (int m = 0; m < M; ++m) xi[m][0] = ldv<NT>(a.recv[left], vi[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (!ok[m]) continue;
+            Acc loc[E], in[E];
+            F::unpack(xl[m], loc);
+            if (from_ws) {
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    from_bits(xi[m][j].x, in[4 * j + 0]);
+                    from_bits(xi[m][j].y, in[4 * j + 1]);
+                    from_bits(xi[m][j].z, in[4 * j + 2]);
+                    from_bits(xi[m][j].w, in[4 * j + 3]);
+                }
+            } else {
+                F::unpack(xi[m][0], in);
+            }
+#pragma unroll
+            for (int j = 0; j < E; ++j) loc[j] = combine<OP>(loc[j], in[j]);
+            if (a.last) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) loc[j] = finalize<OP>(loc[j], n);
+                if (a.scatter) stv<NT>(a.recv[c], vi[m] - v0, F::pack(loc));
+                else stv<NT>(a.recv[r], vi[m], F::pack(loc));
+            } else if (a.ws) {
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    const u32x4 w{to_bits(loc[4 * j + 0]), to_bits(loc[4 * j + 1]), to_bits(loc[4 * j + 2]),
+                                  to_bits(loc[4 * j + 3])};
+                    stv<NT>(a.ws, vi[m] * W + j, w);
+                }
+            } else {
+                stv<NT>(a.recv[r], vi[m], F::pack(loc));
+            }
+        }
+    }
+}
+
+// M = 0: one vector per thread per grid-stride step; M > 0: rs_step_tiles
+// (16-byte vectors only), NT selecting non-temporal access.
+template <class F, int OP, bool VEC, bool NT = false, int M = 0>
 __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
 {
     using Acc = typename F::Acc;
@@ -847,7 +922,8 @@ __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
         // needs q % E == 0, which the host checks.
         const uint64_t v0 = (lo + E - 1) / E, v1 = hi / E;
         const uint64_t nv = v1 > v0 ? v1 - v0 : 0;
-        for (uint64_t v = t0; v < nv; v += stride) {
+        if constexpr (M > 0) rs_step_tiles<F, OP, NT, M>(a, r, left, c, v0, nv);
+        for (uint64_t v = t0; M == 0 && v < nv; v += stride) {
             const uint64_t vi = v0 + v;
             Acc loc[E], in[E];
             F::unpack(ld16(a.send[r], vi), loc);
@@ -883,7 +959,10 @@ __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
 
 // Copy step s of a ring: rank r copies chunk (r - s - shift) mod n from rank
 // r-1 (all-gather phase [handbook, section 环形 all-reduce 与通信量]).
-template <bool VEC>
+// M = 0: one vector per thread per grid-stride step; M > 0 (16-byte vectors
+// only): M vectors a kBlock apart per thread and tile, loads before stores,
+// one workgroup per tile; NT selects non-temporal access.
+template <bool VEC, bool NT = false, int M = 0>
 __global__ __launch_bounds__(kBlock) void copy_step(const CopyArgs a)
 {
     const int n = a.n;
@@ -903,7 +982,23 @@ __global__ __launch_bounds__(kBlock) void copy_step(const CopyArgs a)
         // size, at least 2)
         const uint64_t v0 = (lo + 15) / 16, v1 = hi / 16;
         const uint64_t nv = v1 > v0 ? v1 - v0 : 0;
-        for (uint64_t v = t0; v < nv; v += stride) st16(dst, v0 + v, ld16(src, v0 + v));
+        if constexpr (M > 0) {
+            const uint64_t ntiles = (nv + M * kBlock - 1) / (M * kBlock);
+            for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+                u32x4 x[M];
+                uint64_t vv[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    vv[m] = (t * M + m) * kBlock + threadIdx.x;
+                    x[m] = ldv<NT>(src, v0 + (vv[m] < nv ? vv[m] : 0));  // lanes past the chunk reload its first vector
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    if (vv[m] < nv) stv<NT>(dst, v0 + vv[m], x[m]);
+            }
+        } else {
+            for (uint64_t v = t0; v < nv; v += stride) st16(dst, v0 + v, ld16(src, v0 + v));
+        }
         if (blockIdx.x != 0) return;
         const uint64_t head_end = v0 * 16 < hi ? v0 * 16 : hi;
         const uint64_t tail_start = v1 * 16 > head_end ? v1 * 16 : head_end;
@@ -1486,22 +1581,29 @@ hipError_t fused_op(const ReduceArgs& a, ar_op_t op, bool vec, bool nt, int rank
 }
 
 template <class F, int OP>
-hipError_t rs_vec(const StepArgs& a, bool vec, dim3 grid, hipStream_t s)
+hipError_t rs_vec(const StepArgs& a, bool vec, int tiles, bool nt, dim3 grid, hipStream_t s)
 {
-    if (vec) hipLaunchKernelGGL((rs_step<F, OP, true>), grid, dim3(kBlock), 0, s, a);
-    else hipLaunchKernelGGL((rs_step<F, OP, false>), grid, dim3(kBlock), 0, s, a);
+    if (tiles > 0) {
+        if (!vec || tiles != kStepTiles) return hipErrorInvalidValue;
+        if (nt) hipLaunchKernelGGL((rs_step<F, OP, true, true, kStepTiles>), grid, dim3(kBlock), 0, s, a);
+        else hipLaunchKernelGGL((rs_step<F, OP, true, false, kStepTiles>), grid, dim3(kBlock), 0, s, a);
+    } else if (vec) {
+        hipLaunchKernelGGL((rs_step<F, OP, true>), grid, dim3(kBlock), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((rs_step<F, OP, false>), grid, dim3(kBlock), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 template <class F>
-hipError_t rs_op(const StepArgs& a, ar_op_t op, bool vec, dim3 grid, hipStream_t s)
+hipError_t rs_op(const StepArgs& a, ar_op_t op, bool vec, int tiles, bool nt, dim3 grid, hipStream_t s)
 {
     switch (op) {
-    case AR_SUM: return rs_vec<F, AR_SUM>(a, vec, grid, s);
-    case AR_AVG: return rs_vec<F, AR_AVG>(a, vec, grid, s);
-    case AR_MAX: return rs_vec<F, AR_MAX>(a, vec, grid, s);
-    case AR_MIN: return rs_vec<F, AR_MIN>(a, vec, grid, s);
-    case AR_PROD: return rs_vec<F, AR_PROD>(a, vec, grid, s);
+    case AR_SUM: return rs_vec<F, AR_SUM>(a, vec, tiles, nt, grid, s);
+    case AR_AVG: return rs_vec<F, AR_AVG>(a, vec, tiles, nt, grid, s);
+    case AR_MAX: return rs_vec<F, AR_MAX>(a, vec, tiles, nt, grid, s);
+    case AR_MIN: return rs_vec<F, AR_MIN>(a, vec, tiles, nt, grid, s);
+    case AR_PROD: return rs_vec<F, AR_PROD>(a, vec, tiles, nt, grid, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1607,7 +1709,7 @@ hipError_t multi_op(const MultiArgs& a, ar_op_t op, bool nt, bool rank_major, in
 #define AR_RING_INSTANTIATIONS(F, EXTERN)                                                                       \
     EXTERN template hipError_t fused_op<F, true>(const ReduceArgs&, ar_op_t, bool, bool, int, dim3, hipStream_t);  \
     EXTERN template hipError_t fused_op<F, false>(const ReduceArgs&, ar_op_t, bool, bool, int, dim3, hipStream_t); \
-    EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, dim3, hipStream_t);                       \
+    EXTERN template hipError_t rs_op<F>(const StepArgs&, ar_op_t, bool, int, bool, dim3, hipStream_t);            \
     EXTERN template hipError_t multi_op<F>(const MultiArgs&, ar_op_t, bool, bool, int, hipStream_t);
 #define AR_TREE_INSTANTIATIONS(F, EXTERN)                                                           \
     EXTERN template hipError_t tree_op<F>(const ReduceArgs&, ar_op_t, bool, bool, dim3, hipStream_t); \

@@ -489,3 +489,63 @@ def test_all_gather_rank_major_full_compare(n, dtype, sc, inplace):
         del send, recv
     del xs
     free()
+
+
+# Ring steps take their tiled form (four vectors per thread and tile, one
+# workgroup per tile) once a step has at least 8 tiles per CU: at 256 CUs,
+# chunks of 2048/N tiles of 4 KiB or more. These sizes clear that with
+# chunks that start inside a vector; fp32/int32 beyond the last-level cache
+# stream, fp16/bf16 partials in the fp32 workspace stay cached.
+@pytest.mark.parametrize("n,dtype,op,count,inplace,mode", [
+    (8, "f32", "sum", 9_000_005, False, "stepwise"),
+    (3, "f16", "avg", 64_000_007, True, "stepwise"),
+    (5, "bf16", "max", 40_000_003, False, "stepwise"),
+    (4, "i32", "prod", 9_000_001, True, "stepwise"),
+    (8, "f32", "min", 9_000_005, True, "graph"),
+])
+def test_tiled_ring_steps_all_reduce(n, dtype, op, count, inplace, mode):
+    """The ring's reduce-scatter and all-gather steps in their tiled form:
+    every element of every rank against the oracle, guard bands."""
+    with ar.Comm(n, 0) as comm:
+        ws = gu.attach_workspace(comm, ar.AR_COLL_ALL_REDUCE, n, count, dtype, mode)
+        xs = gu.make_inputs(n, count, dtype, op, seed=n * 7 + count % 13)
+        exp = gu.oracle_all_reduce(xs, dtype, op)
+        got, send, recv = gu.run_all_reduce(comm, xs, dtype, op, mode, inplace=inplace)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"{mode} n={n} {dtype} {op} count={count} inplace={inplace} rank {r}")
+        ar.ar_comm_set_workspace(comm, None)
+        del ws, xs, exp, got, send, recv
+    free()
+
+
+@pytest.mark.parametrize("n,dtype,op,rc,inplace", [(8, "f32", "sum", 1_100_000, False),
+                                                   (4, "f16", "avg", 4_400_000, True),
+                                                   (3, "i32", "max", 2_800_004, False)])
+def test_tiled_ring_steps_reduce_scatter(n, dtype, op, rc, inplace):
+    """The stepwise reduce-scatter in its tiled form (partials in the
+    workspace): every element of every rank's block against the oracle."""
+    from test_gpu_parity import _reduce_scatter
+    xs = gu.make_inputs(n, n * rc, dtype, op, seed=n + rc % 101)
+    exp = oracle.reduce_scatter([gu.host(x) for x in xs], dtype, op)
+    with ar.Comm(n, 0) as comm:
+        got = _reduce_scatter(comm, xs, dtype, op, "stepwise", inplace)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"RS stepwise n={n} {dtype} {op} rc={rc} inplace={inplace} rank {r}")
+    del xs, exp, got
+    free()
+
+
+@pytest.mark.parametrize("n,dtype,sc,inplace", [(8, "f16", 2_200_000, False), (3, "f32", 3_000_004, True)])
+def test_tiled_ring_steps_all_gather(n, dtype, sc, inplace):
+    """The stepwise all-gather's copy steps in their tiled form: every output
+    block of every rank bit for bit against its input block."""
+    from test_gpu_parity import _all_gather
+    xs = gu.make_inputs(n, sc, dtype, "sum", seed=sc % 89)
+    with ar.Comm(n, 0) as comm:
+        got = _all_gather(comm, xs, dtype, "stepwise", inplace)
+    iv = np.int16 if gu.ESIZE[dtype] == 2 else np.int32
+    for r in range(n):
+        for p in range(n):
+            assert np.array_equal(got[r][p * sc:(p + 1) * sc].view(iv), gu.host(xs[p]).view(iv)), (r, p)
+    del xs, got
+    free()
