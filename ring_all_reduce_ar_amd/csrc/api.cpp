@@ -688,11 +688,17 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
         a.count = count;
         a.q = count;
         a.n = n;
-        // one row over the whole buffer: 16 workgroups per CU up to 128 MiB
-        // per rank or at 32+ ranks, 8 above (measured ±2-3% at 8 ranks)
+        // One row over the whole buffer. Streaming (16-byte vectors): one
+        // workgroup per 256-vector tile, in order (against 8-16 per CU on the
+        // same buffers: 8 x 256 MiB fp32 0.823 -> 0.727 ms, 8 x 1 GiB fp16
+        // 3.62 -> 3.00 ms, 16 x 128 MiB 0.796 -> 0.762 ms, 5 x 256 MiB 0.517 ->
+        // 0.481 ms). Cached: 16 workgroups per CU up to 128 MiB per rank or
+        // at 32+ ranks, 8 above (measured ±2-3% at 8 ranks).
         const int per_cu = (count * e <= (size_t(128) << 20) || n >= 32) ? 16 : 8;
-        const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, per_cu);
         const bool nt = call_nt(comm, footprint(n, sendbufs, recvbufs, count * e, count * e), kLastLevelCacheBytes);
+        const int gx = aligned && nt ? static_cast<int>(std::clamp<uint64_t>(
+                                           ceil_div(ceil_div(count, epv), static_cast<uint64_t>(ar::kBlock)), 1, kMaxGridX))
+                                     : grid_for(comm, aligned ? ceil_div(count, epv) : count, 1, per_cu);
         return run_eager(comm, stream, 1, [&](hipStream_t s, StepTimer* t) {
             hipError_t err = ar::launch_tree_fused(a, dtype, op, aligned, nt, gx, s);
             return err != hipSuccess ? err : tick(t);
@@ -706,7 +712,14 @@ ar_result_t tree_all_reduce(ar_comm* comm, const void* const sendbufs[], void* c
     ta.ws_stride = (count + 3) / 4 * 4;
     ta.count = count;
     ta.n = n;
-    const int gx = grid_for(comm, aligned ? ceil_div(count, epv) : count, std::max(1, n / 2));
+    // The levels' grid: beyond the last-level cache one workgroup per
+    // 256-vector tile of a pair row (8 x 256 MiB fp32 1.805 -> 1.511 ms, fp16
+    // 2.443 -> 2.109 ms, 16 x 128 MiB 1.960 -> 1.610 ms against 8 per CU),
+    // else 8 workgroups per CU over the pairs.
+    const bool lvl_exact = aligned && use_nt(footprint(n, sendbufs, recvbufs, count * e, count * e));
+    const int gx = lvl_exact ? static_cast<int>(std::clamp<uint64_t>(
+                                   ceil_div(ceil_div(count, epv), static_cast<uint64_t>(ar::kBlock)), 1, kMaxGridX))
+                             : grid_for(comm, aligned ? ceil_div(count, epv) : count, std::max(1, n / 2));
     const bool bvec = aligned;
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int l = 0; l < levels; ++l) {
@@ -1079,11 +1092,15 @@ AR_EXPORT ar_result_t ar_all_to_all(ar_comm_t comm, const void* const sendbufs[]
             return err != hipSuccess ? err : tick(t);
         });
     }
-    const int gx = grid_for(comm, units, n);
+    // Each step moves N block pairs; streaming steps with at least 8 tiles
+    // per CU take the tiled copy, one workgroup per tile.
+    const int tiles = vec ? copy_tile_grid(blk / 16) : 0;
+    const bool tiled = vec && nt && static_cast<uint64_t>(tiles) * n >= static_cast<uint64_t>(comm->num_cus) * 8;
+    const int gx = tiled ? tiles : grid_for(comm, units, n);
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int st = 0; st < n; ++st) {
             a.step = st;
-            hipError_t err = ar::launch_all_to_all(a, vec, nt, false, gx, s);
+            hipError_t err = ar::launch_all_to_all(a, vec, nt, tiled, gx, s);
             if (err == hipSuccess) err = tick(t);
             if (err != hipSuccess) return err;
         }

@@ -202,22 +202,24 @@ def test_grad7b_reduce_scatter_then_all_gather():
     free()
 
 
-@pytest.mark.parametrize("n,dtype,blk", [(2, "f32", 20_000_004), (4, "f16", 9_000_008), (16, "bf16", 600_008),
-                                         (5, "f32", 3_000_004)])
-def test_all_to_all_tiled_full_compare(n, dtype, blk):
-    """Beyond the last-level cache the fused all-to-all takes the tiled copy
-    (four vectors per thread, one workgroup per tile, ragged last tiles):
-    every element of every rank against the oracle's transpose."""
+@pytest.mark.parametrize("n,dtype,blk,mode", [(2, "f32", 20_000_004, "fused"), (4, "f16", 9_000_008, "fused"),
+                                              (16, "bf16", 600_008, "fused"), (5, "f32", 3_000_004, "fused"),
+                                              (8, "f32", 1_200_004, "stepwise"), (3, "f16", 8_000_008, "stepwise")])
+def test_all_to_all_tiled_full_compare(n, dtype, blk, mode):
+    """Beyond the last-level cache the all-to-all takes the tiled copy (four
+    vectors per thread, one workgroup per tile, ragged last tiles), in one
+    launch or one per ring step: every element of every rank against the
+    oracle's transpose."""
     assert 2 * n * n * blk * gu.ESIZE[dtype] > 256 << 20
     xs = gu.make_inputs(n, n * blk, dtype, "sum", seed=n + blk % 97)
     exp = oracle.all_to_all([gu.host(x) for x in xs], dtype)
     with ar.Comm(n, 0) as comm:
         recv = [gu.RankBuf(n * blk, dtype) for _ in range(n)]
-        ar.ar_all_to_all(comm, [x.data_ptr() for x in xs], [b.ptr() for b in recv], blk, dtype, "fused")
+        ar.ar_all_to_all(comm, [x.data_ptr() for x in xs], [b.ptr() for b in recv], blk, dtype, mode)
         torch.cuda.synchronize()
         for p in range(n):
             assert recv[p].guards_ok(), f"rank {p} guard"
-            gu.assert_same(gu.host(recv[p].view), exp[p], dtype, f"all-to-all n={n} {dtype} blk={blk} rank {p}")
+            gu.assert_same(gu.host(recv[p].view), exp[p], dtype, f"all-to-all {mode} n={n} {dtype} blk={blk} rank {p}")
         del recv
     del xs, exp
     free()

@@ -42,6 +42,32 @@ def test_tree_parity(n, dtype, mode):
                                                               f"inplace={inplace} rank {r}")
 
 
+@pytest.mark.parametrize("n,dtype,op,count,mode,inplace", [
+    (8, "f32", "sum", 9_000_003, "tree", False),
+    (5, "bf16", "avg", 30_000_005, "tree", True),
+    (16, "f32", "max", 5_000_001, "tree", False),
+    (8, "f16", "prod", 20_000_003, "tree_stepwise", False),
+    (7, "f32", "min", 10_000_001, "tree_stepwise", True),
+    (33, "i32", "sum", 2_000_003, "tree_stepwise", False),
+])
+def test_tree_streaming_full_compare(n, dtype, op, count, mode, inplace):
+    """Beyond the last-level cache the tree kernels launch one workgroup per
+    tile of 256 vectors (tail elements past the last whole vector): every
+    element of every rank against the oracle's tree, guard bands."""
+    with ar.Comm(n, 0) as comm:
+        xs = gu.make_inputs(n, count, dtype, op, seed=n + count % 53)
+        exp = oracle.tree_all_reduce([gu.host(x) for x in xs], dtype, op)
+        ws = gu.attach_workspace(comm, ar.AR_COLL_ALL_REDUCE, n, count, dtype, mode)
+        outs, _, _ = gu.run_all_reduce(comm, xs, dtype, op, mode, inplace=inplace)
+        ar.ar_comm_set_workspace(comm, None)
+        del ws
+        for r in range(n):
+            gu.assert_same(outs[r], exp[r], dtype, f"tree n={n} {dtype} {op} {mode} count={count} inplace={inplace} "
+                                                  f"rank {r}")
+    del xs, exp, outs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ("f32", "f16", "bf16"))
 @pytest.mark.parametrize("n", (8, 64))
 def test_tree_within_tolerance_of_ring(n, dtype):
