@@ -497,3 +497,75 @@ def test_multi_at_the_tensor_limit():
         with pytest.raises(ar.ArError) as ei:
             ar.ar_all_reduce_multi(comm, rows + rows[:1], rows + rows[:1], [per] * (t + 1), "f32", "sum")
         assert ei.value.code == ar.AR_ERR_INVALID_ARGUMENT
+
+
+def _views_case(n, sizes, dtype, op, seed, layout, inplace):
+    """Tensors as views into one send (and one recv) allocation per rank, at
+    the same offsets on every rank. layout: "gapped" (tensor order, a few
+    elements between tensors), "shuffled" (memory order differs from tensor
+    order, tensor 0 lowest), "base_not_first" (tensor 0 in the middle).
+    Returns (flat inputs, outputs per rank in tensor order)."""
+    e = gu.ESIZE[dtype]
+    total = sum(sizes)
+    flat = gu.make_inputs(n, total, dtype, op, seed=seed)
+    order = list(range(len(sizes)))
+    if layout == "shuffled":
+        rest = order[1:]
+        np.random.default_rng(seed).shuffle(rest)
+        order = [0] + rest
+    elif layout == "base_not_first":
+        order = order[1:len(order) // 2 + 1] + [0] + order[len(order) // 2 + 1:]
+    where, pos = {}, 0
+    for t in order:
+        pos += 3 + (t % 5)  # a gap of a few elements before every tensor
+        where[t] = pos
+        pos += sizes[t]
+    span = pos + 8
+    send = [gu.RankBuf(span, dtype, offset=2 * e) for _ in range(n)]
+    recv = send if inplace else [gu.RankBuf(span, dtype, offset=2 * e) for _ in range(n)]
+    off = 0
+    for t, c in enumerate(sizes):
+        for r in range(n):
+            send[r].view[where[t]:where[t] + c].copy_(flat[r][off:off + c])
+        off += c
+    rows_s = [[send[r].sub_ptr(where[t]) for r in range(n)] for t in range(len(sizes))]
+    rows_r = [[recv[r].sub_ptr(where[t]) for r in range(n)] for t in range(len(sizes))]
+    return flat, send, recv, rows_s, rows_r, where
+
+
+@pytest.mark.parametrize("n,dtype,op,layout,inplace,total_mib", [
+    (8, "f32", "sum", "gapped", True, 1), (8, "bf16", "avg", "shuffled", False, 1),
+    (3, "f16", "max", "gapped", False, 1), (64, "f32", "min", "shuffled", True, 1),
+    (5, "i32", "prod", "base_not_first", True, 1), (8, "f32", "sum", "gapped", False, 48),
+    (8, "f16", "avg", "shuffled", True, 40), (64, "f32", "max", "gapped", True, 6),
+])
+def test_multi_views_layouts(n, dtype, op, layout, inplace, total_mib):
+    """Tensors as views at one offset into every rank's allocation, cached and
+    streaming sizes: gaps between tensors, memory order unlike tensor order
+    (the ring chunks follow tensor order), tensor 0 in the middle, out of
+    place. Every element against the oracle's fold over the bucket in tensor
+    order, and bit for bit against the flat call on a packed copy."""
+    e = gu.ESIZE[dtype]
+    rng = np.random.default_rng(n + total_mib)
+    target = (total_mib << 20) // e
+    sizes = []
+    while sum(sizes) < target:
+        sizes.append(int(rng.integers(1, max(2, target // 6))))
+    sizes += [0, 7]
+    flat, send, recv, rows_s, rows_r, where = _views_case(n, sizes, dtype, op, seed=n * 3 + total_mib, layout=layout,
+                                                          inplace=inplace)
+    with ar.Comm(n, 0) as comm:
+        ar.ar_all_reduce_multi(comm, rows_s, rows_r, sizes, dtype, op)
+        torch.cuda.synchronize()
+        packed = [x.clone() for x in flat]
+        pp = [b.data_ptr() for b in packed]
+        ar.ar_all_reduce(comm, pp, pp, sum(sizes), dtype, op, "fused")
+        torch.cuda.synchronize()
+    exp = gu.oracle_all_reduce(flat, dtype, op)
+    for r in range(n):
+        assert recv[r].guards_ok() and send[r].guards_ok(), f"rank {r} guard"
+        got = np.concatenate([gu.host(recv[r].view[where[t]:where[t] + c]) for t, c in enumerate(sizes)])
+        gu.assert_same(got, exp[r], dtype, f"views n={n} {dtype} {op} {layout} inplace={inplace} rank {r}")
+        gu.assert_same(got, gu.host(packed[r]), dtype, f"views vs flat rank {r}")
+    del flat, send, recv, packed
+    torch.cuda.empty_cache()
