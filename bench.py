@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grad7b]
                     [--mode fused|stepwise|graph|tree|tree_stepwise]
                     [--collective all_reduce|reduce_scatter|all_gather|all_to_all]
-                    [--multi] [--access auto|streaming|cached] [--no-cpu-baseline]
+                    [--op OP] [--multi] [--access auto|streaming|cached] [--no-cpu-baseline]
     python bench.py --sweep            # 1 KiB..256 MiB per rank, every mode, alpha-beta fit
     python bench.py --copy-probe BYTES # a plain device copy (HBM counter calibration)
 
@@ -541,6 +541,8 @@ def main():
                     help="the collective to time on the workload's rank buffers: reduce_scatter takes count "
                          "elements per rank in and count/N out, all_gather count/N in and count out, all_to_all "
                          "count in and out (out of place)")
+    ap.add_argument("--op", default=None, choices=["sum", "avg", "max", "min", "prod"],
+                    help="reduction op instead of the workload's own (all-reduce, reduce-scatter)")
     ap.add_argument("--multi", action="store_true",
                     help="bucket64/bucket8: reduce the bucket as its mixed-size tensors with ar_all_reduce_multi")
     ap.add_argument("--access", default="auto", choices=["auto", "streaming", "cached"],
@@ -599,6 +601,9 @@ def main():
     if args.mode is None:
         args.mode = "stepwise" if args.workload == "small" else "fused"
     n, count, dtype, op, desc = WORKLOADS[args.workload]
+    if args.op and args.op != op:
+        op = args.op
+        desc += f"; op {op.upper()} instead"
     wl = {"bucket8": "bucket64"}.get(args.workload, args.workload)
     wl = wl if wl in synthetic.WORKLOAD_IDS else "sweep"
     comm = ar.Comm(n, 0)
@@ -724,7 +729,9 @@ def main():
     alg_bytes = (2 * n if coll in ("all_reduce", "all_to_all") else n + 1) * s_bytes
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     # counter summaries cover the default access rule and the flat call
-    traffic = None if args.multi or args.access != "auto" else load_traffic(args.workload, args.mode, coll)
+    # the committed counters belong to the workload's own op, access and layout
+    own = not args.multi and args.access == "auto" and op == WORKLOADS[args.workload][3]
+    traffic = load_traffic(args.workload, args.mode, coll) if own else None
     result = {
         "metric": METRIC,
         "value": sig(algbw),

@@ -92,6 +92,15 @@ def test_bench_line_small_stepwise_steps():
     assert rs["alpha_call_us"] == pytest.approx(j["ms_per_step"] * 1e3 / (2 * (n - 1)), rel=1e-3, abs=1e-3)
 
 
+def test_bench_line_op_override():
+    """--op replaces the workload's reduction op; the line names it, and
+    reports no HBM-counter traffic (the committed counters are for the
+    workload's own op)."""
+    j = run_bench("--workload", "small", "--op", "prod", "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    assert j["config"]["op"] == "prod" and "PROD" in j["config"]["workload"]
+    assert j["roofline"]["traffic"] is None
+
+
 def test_range_point_fields():
     """One point of the metric-range block the default line carries."""
     import torch
