@@ -200,10 +200,11 @@ bool use_nt(uint64_t footprint_bytes) { return footprint_bytes > kLastLevelCache
 // calls gain more from non-temporal access than warm ones lose: 8 ranks,
 // fp32, cold (every call from HBM) / warm (repeated on one buffer set), in
 // microseconds, cached two-tile against non-temporal rank-major kernels:
-// 16 MiB per rank 57.8 / 41.4 against 53.0 / 50.1 (below the threshold);
-// 20 MiB 71.5 / 50.4 against 61.0 / 58.6; 25 MiB 86.3 / 61.5 against
-// 73.2 / 70.6; 32 MiB 108.6 / 78.1 against 87.4 / 85.6. Streaming wins
-// unless the data is warm more than 55-75% of the time.
+// 16 MiB per rank 59.4 / 41.0 against 48.7 / 48.1 (at the threshold, stays
+// cached); 20 MiB 71.6 / 50.0 against 61.1 / 60.0; 25 MiB 87.0 / 62.1
+// against 75.2 / 73.6. Streaming wins there unless the data is warm more
+// than about half the time; at 16 ranks x 8 MiB it loses cold too (56.7
+// against 60.6), which the threshold keeps cached.
 constexpr uint64_t kAllReduceStreamBytes = kLastLevelCacheBytes / 2;
 
 // The access flavour of a one-launch call (ar_comm_set_access): AUTO streams
