@@ -708,11 +708,13 @@ def main():
         torch.cuda.empty_cache()
         return ms_, per_step, warm, ring_steps, sbc
 
-    # The first allocation of the rank buffers in a fresh process measured up
-    # to ~9% slower on MI355X than the same buffers allocated again after a
-    # free (same virtual addresses, different physical backing). Both passes
-    # are timed; the second is the steady state a long-running job sees and
-    # is the reported value; the first is reported beside it.
+    # In the first process on a freshly started MI355X, the first allocation
+    # of the rank buffers measured 3-7% slower than the same buffers allocated
+    # again after a free to the driver (same virtual addresses): the same
+    # requests, evenly spread over the L2 channels, with fewer of them in
+    # flight toward memory. Both passes are timed; the second is the steady
+    # state a long-running job sees and is the reported value; the first is
+    # reported beside it.
     first_ms = timed_pass(False)[0]
     ms, per_step, warm_ms, ring_steps, sbc_ms = timed_pass(True)
     per_step.sort()
