@@ -289,28 +289,32 @@ int rank_major_scatter_grid(uint64_t q, size_t elem, int m)
 // workgroup per tile) when a step has at least 8 such workgroups per CU, else
 // one vector (or unit) per thread over 8 workgroups per CU. `vecs`: whole
 // 16-byte vectors per chunk; `units`: the untiled kernel's work items per
-// chunk; `nt_ok`: the step may stream (non-temporal) beyond the last-level
-// cache. Against the untiled steps on the same buffers (stepwise mode):
+// chunk. Tiled steps stream (non-temporal) when the call's footprint exceeds
+// the last-level cache. Against the untiled steps on the same buffers (stepwise mode):
 // fp32 8 x 256 MiB 1.744 -> 1.491 ms (non-temporal; 1.644 cached), 4 x
 // 256 MiB 0.746 -> 0.647 ms, 2 x 512 MiB 0.532 -> 0.430 ms, 16 x 128 MiB
 // 1.749 -> 1.643 ms, the graph mode 8 x 256 MiB 1.732 -> 1.499 ms;
 // reduce-scatter 8 x 256 MiB in 1.035 -> 0.927 ms; all-gather 8 x 32 MiB in
-// 0.771 -> 0.691 ms. fp16 partials in the fp32 workspace stay cached: 8 x
-// 256 MiB 2.318 -> 2.116 ms cached against 2.437 non-temporal, 8 x 7e9
-// 126.9 -> 120.5 against 141.3 ms, the reduce-scatter 1.632 -> 1.524 against
-// 1.839 ms.
+// 0.771 -> 0.691 ms. The 16-bit steps, whose partials are fp32 in the
+// workspace, tile by half vectors (rs_step_halves), so that a wave's partial
+// loads cover whole lines and the partials stream as well: against
+// whole-vector tiles with cached partials (streaming partials there cost
+// 15-20%), fp16 8 x 256 MiB 2.117 -> 2.046 ms, 8 x 7e9 120.3 -> 116.4 ms
+// (MAX; AVG 118.8 -> 115.9), the reduce-scatter 8 x 16.8M out 1.520 -> 1.446
+// ms, 8 x 875M out 84.7 -> 81.7 ms; half vectors with cached partials 2.153,
+// 120.2, 1.558, 83.1 ms.
 struct StepShape {
     int tiles;  // 0 or ar::kStepTiles
     bool nt;
     int grid_x;
 };
 StepShape step_shape(const ar_comm* comm, bool vec, uint64_t vecs, uint64_t units, int nranks,
-                     uint64_t footprint_bytes, bool nt_ok)
+                     uint64_t footprint_bytes)
 {
     const uint64_t tiles = ceil_div(vecs + 1, static_cast<uint64_t>(ar::kStepTiles) * ar::kBlock);
     if (!vec || tiles * static_cast<uint64_t>(nranks) < static_cast<uint64_t>(comm->num_cus) * 8)
         return {0, false, grid_for(comm, units, nranks)};
-    return {ar::kStepTiles, nt_ok && use_nt(footprint_bytes), static_cast<int>(std::clamp<uint64_t>(tiles, 1, kMaxGridX))};
+    return {ar::kStepTiles, use_nt(footprint_bytes), static_cast<int>(std::clamp<uint64_t>(tiles, 1, kMaxGridX))};
 }
 
 // Workgroups per row for the tiled copies (all-gather, all-to-all): one per
@@ -809,9 +813,8 @@ ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* 
     sa.q = q;
     sa.n = n;
     sa.scatter = 0;
-    const bool ws16 = sa.ws != nullptr;
     const uint64_t foot = footprint(n, sendbufs, recvbufs, bytes, bytes);
-    const StepShape rs_shape = step_shape(comm, vec, ceil_div(q, epv), vec ? ceil_div(q, epv) : q, n, foot, !ws16);
+    const StepShape rs_shape = step_shape(comm, vec, ceil_div(q, epv), vec ? ceil_div(q, epv) : q, n, foot);
     // All-gather: n-1 copy steps; step s moves chunk (r - s) mod n from rank r-1 to rank r.
     ar::CopyArgs ca{};
     for (int r = 0; r < n; ++r) ca.recv[r] = recvbufs[r];
@@ -821,7 +824,7 @@ ar_result_t all_reduce_impl(ar_comm_t comm, const void* const sendbufs[], void* 
     ca.shift = 0;
     const bool cvec = vec;
     const StepShape ag_shape =
-        step_shape(comm, cvec, ceil_div(ca.qb, 16), cvec ? ceil_div(ca.qb, 16) : ceil_div(ca.qb, 2), n, foot, true);
+        step_shape(comm, cvec, ceil_div(ca.qb, 16), cvec ? ceil_div(ca.qb, 16) : ceil_div(ca.qb, 2), n, foot);
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int st = 0; st < n - 1; ++st) {
             sa.s = st;
@@ -941,8 +944,7 @@ AR_EXPORT ar_result_t ar_reduce_scatter(ar_comm_t comm, const void* const sendbu
     sa.n = n;
     sa.scatter = 1;
     const StepShape shape = step_shape(comm, vec, ceil_div(q, epv), vec ? ceil_div(q, epv) : q, n,
-                                       footprint(n, sendbufs, recvbufs, sbytes, rbytes),
-                                       e != 2);
+                                       footprint(n, sendbufs, recvbufs, sbytes, rbytes));
     Enqueue fn = [=](hipStream_t s, StepTimer* t) mutable {
         for (int st = 0; st < n - 1; ++st) {
             sa.s = st;
@@ -983,7 +985,7 @@ AR_EXPORT ar_result_t ar_all_gather(ar_comm_t comm, const void* const sendbufs[]
         std::fprintf(stderr, "[allreduce] all_gather n=%d sendcount=%zu dtype=%s mode=%d vec=%d\n", n, sendcount,
                      dtype_name(dtype), static_cast<int>(mode), vec ? 1 : 0);
     const StepShape shape = step_shape(comm, vec, ceil_div(blk, 16), vec ? ceil_div(blk, 16) : ceil_div(blk, 2), n,
-                                       footprint(n, sendbufs, recvbufs, blk, rbytes), true);
+                                       footprint(n, sendbufs, recvbufs, blk, rbytes));
 
     if (!stepwise) {
         ar::CopyArgs a{};

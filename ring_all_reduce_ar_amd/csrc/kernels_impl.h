@@ -27,6 +27,7 @@ namespace ar {
 namespace detail {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Rank buffers are global memory. Pointers that come from kernel arguments
 // are known to be global; pointers read from a device-memory table are not,
@@ -128,6 +129,18 @@ struct F16 {
         for (int j = 0; j < 4; ++j) w[j] = f32_to_half(a[2 * j]) | (f32_to_half(a[2 * j + 1]) << 16);
         return u32x4{w[0], w[1], w[2], w[3]};
     }
+    // half a vector: four elements in 8 bytes, in the order unpack uses
+    static __device__ __forceinline__ void unpack4(u32x2 v, Acc* a)
+    {
+        a[0] = half_to_f32(v.x & 0xFFFFu);
+        a[1] = half_to_f32(v.x >> 16);
+        a[2] = half_to_f32(v.y & 0xFFFFu);
+        a[3] = half_to_f32(v.y >> 16);
+    }
+    static __device__ __forceinline__ u32x2 pack4(const Acc* a)
+    {
+        return u32x2{f32_to_half(a[0]) | (f32_to_half(a[1]) << 16), f32_to_half(a[2]) | (f32_to_half(a[3]) << 16)};
+    }
 };
 
 struct BF16 {
@@ -156,6 +169,17 @@ struct BF16 {
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16(a[2 * j]) | (f32_to_bf16(a[2 * j + 1]) << 16);
         return u32x4{w[0], w[1], w[2], w[3]};
+    }
+    static __device__ __forceinline__ void unpack4(u32x2 v, Acc* a)
+    {
+        a[0] = as_f(v.x << 16);
+        a[1] = as_f(v.x & 0xFFFF0000u);
+        a[2] = as_f(v.y << 16);
+        a[3] = as_f(v.y & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ u32x2 pack4(const Acc* a)
+    {
+        return u32x2{f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16), f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16)};
     }
 };
 
@@ -248,6 +272,20 @@ template <bool NT>
 __device__ __forceinline__ void stv_at(void* base, uint64_t byte_off, u32x4 x)
 {
     stv<NT>(static_cast<char*>(base) + byte_off, 0, x);
+}
+
+// 8-byte units (half a vector of a 16-bit type).
+template <bool NT>
+__device__ __forceinline__ u32x2 ldh(const void* base, uint64_t h)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(gptr<u32x2>(base) + h);
+    else return gptr<u32x2>(base)[h];
+}
+template <bool NT>
+__device__ __forceinline__ void sth(void* base, uint64_t h, u32x2 x)
+{
+    if constexpr (NT) __builtin_nontemporal_store(x, gptr<u32x2>(base) + h);
+    else gptr<u32x2>(base)[h] = x;
 }
 
 __device__ __forceinline__ int wrap_rank(int r, int n) { return r >= n ? r - n : r; }
@@ -899,8 +937,75 @@ __device__ __forceinline__ void rs_step_tiles(const StepArgs& a, int r, int left
     }
 }
 
+// The tiled step for the 16-bit types, whose partials between steps are fp32
+// in the workspace (16 bytes per 8 bytes of data; workspace vector 2v + h
+// holds elements 4h..4h+3 of data vector v). The threads take half vectors:
+// 2M per thread and tile, lane l of a wave half l of each run of 64, so each
+// load and store instruction of a wave covers one contiguous run (512 bytes of
+// data, 1 KiB of partials). With a whole data vector per lane, each of its two
+// partial loads would cover every other 16 bytes of 2 KiB. Each element's
+// arithmetic is that of rs_step_tiles.
+template <class F, int OP, bool NT, int M>
+__device__ __forceinline__ void rs_step_halves(const StepArgs& a, int r, int left, int c, uint64_t v0, uint64_t nv)
+{
+    using Acc = typename F::Acc;
+    constexpr int H = 2 * M;
+    const int n = a.n;
+    const uint64_t h0 = 2 * v0, nh = 2 * nv;
+    const uint64_t ntiles = (nh + H * kBlock - 1) / (H * kBlock);
+    const bool from_ws = !a.first && a.ws;
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        uint64_t hv[H];
+        bool ok[H];
+        u32x2 xl[H], xi[H];
+        u32x4 xw[H];
+#pragma unroll
+        for (int m = 0; m < H; ++m) {
+            const uint64_t h = (t * H + m) * kBlock + threadIdx.x;
+            ok[m] = h < nh;
+            hv[m] = h0 + (ok[m] ? h : 0);  // lanes past the chunk reload its first half vector
+            xl[m] = ldh<NT>(a.send[r], hv[m]);
+        }
+        if (from_ws) {
+#pragma unroll
+            for (int m = 0; m < H; ++m) xw[m] = ldv<NT>(a.ws, hv[m]);
+        } else {
+            const void* src = a.first ? a.send[left] : a.recv[left];
+#pragma unroll
+            for (int m = 0; m < H; ++m) xi[m] = ldh<NT>(src, hv[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < H; ++m) {
+            if (!ok[m]) continue;
+            Acc loc[4], in[4];
+            F::unpack4(xl[m], loc);
+            if (from_ws) {
+                from_bits(xw[m].x, in[0]);
+                from_bits(xw[m].y, in[1]);
+                from_bits(xw[m].z, in[2]);
+                from_bits(xw[m].w, in[3]);
+            } else {
+                F::unpack4(xi[m], in);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) loc[j] = combine<OP>(loc[j], in[j]);
+            if (a.last) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) loc[j] = finalize<OP>(loc[j], n);
+                if (a.scatter) sth<NT>(a.recv[c], hv[m] - h0, F::pack4(loc));
+                else sth<NT>(a.recv[r], hv[m], F::pack4(loc));
+            } else if (a.ws) {
+                stv<NT>(a.ws, hv[m], u32x4{to_bits(loc[0]), to_bits(loc[1]), to_bits(loc[2]), to_bits(loc[3])});
+            } else {
+                sth<NT>(a.recv[r], hv[m], F::pack4(loc));
+            }
+        }
+    }
+}
+
 // M = 0: one vector per thread per grid-stride step; M > 0: rs_step_tiles
-// (16-byte vectors only), NT selecting non-temporal access.
+// (rs_step_halves for the 16-bit types; 16-byte vectors only), NT selecting
+// non-temporal access.
 template <class F, int OP, bool VEC, bool NT = false, int M = 0>
 __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
 {
@@ -922,7 +1027,8 @@ __global__ __launch_bounds__(kBlock) void rs_step(const StepArgs a)
         // needs q % E == 0, which the host checks.
         const uint64_t v0 = (lo + E - 1) / E, v1 = hi / E;
         const uint64_t nv = v1 > v0 ? v1 - v0 : 0;
-        if constexpr (M > 0) rs_step_tiles<F, OP, NT, M>(a, r, left, c, v0, nv);
+        if constexpr (M > 0 && F::kEpv == 8) rs_step_halves<F, OP, NT, M>(a, r, left, c, v0, nv);
+        else if constexpr (M > 0) rs_step_tiles<F, OP, NT, M>(a, r, left, c, v0, nv);
         for (uint64_t v = t0; M == 0 && v < nv; v += stride) {
             const uint64_t vi = v0 + v;
             Acc loc[E], in[E];
