@@ -494,14 +494,16 @@ def test_all_gather_rank_major_full_compare(n, dtype, sc, inplace):
 
 
 # Ring steps take their tiled form (four vectors per thread and tile, one
-# workgroup per tile) once a step has at least 8 tiles per CU: at 256 CUs,
-# chunks of 2048/N tiles of 4 KiB or more. These sizes clear that with
-# chunks that start inside a vector; fp32/int32 beyond the last-level cache
-# stream, fp16/bf16 partials in the fp32 workspace stay cached.
+# workgroup per tile; half vectors per lane for fp16/bf16) once a step has at
+# least 8 tiles per CU: at 256 CUs, chunks of 2048/N tiles of 4 KiB or more.
+# These sizes clear that with chunks that start inside a vector; beyond the
+# last-level cache the steps stream, and 8 x 16,777,003 fp16 in place (a
+# footprint just under the 256 MiB cache) takes the cached half-vector step.
 @pytest.mark.parametrize("n,dtype,op,count,inplace,mode", [
     (8, "f32", "sum", 9_000_005, False, "stepwise"),
     (3, "f16", "avg", 64_000_007, True, "stepwise"),
     (5, "bf16", "max", 40_000_003, False, "stepwise"),
+    (8, "f16", "sum", 16_777_003, True, "stepwise"),
     (4, "i32", "prod", 9_000_001, True, "stepwise"),
     (8, "f32", "min", 9_000_005, True, "graph"),
 ])
@@ -522,6 +524,7 @@ def test_tiled_ring_steps_all_reduce(n, dtype, op, count, inplace, mode):
 
 @pytest.mark.parametrize("n,dtype,op,rc,inplace", [(8, "f32", "sum", 1_100_000, False),
                                                    (4, "f16", "avg", 4_400_000, True),
+                                                   (8, "bf16", "min", 2_100_008, False),
                                                    (3, "i32", "max", 2_800_004, False)])
 def test_tiled_ring_steps_reduce_scatter(n, dtype, op, rc, inplace):
     """The stepwise reduce-scatter in its tiled form (partials in the
