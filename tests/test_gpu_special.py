@@ -107,3 +107,55 @@ def test_int32_wrap_and_truncation(n, mode):
             outs, _, _ = gu.run_all_reduce(comm, xs, "i32", op, mode)
             for r in range(n):
                 gu.assert_same(outs[r], exp[r], "i32", f"n={n} i32 {op} {mode} rank {r}")
+
+
+@pytest.mark.parametrize("n", (3, 8, 16))
+def test_special_values_streaming(n):
+    """Special values through the streaming one-launch kernels (the
+    rank-major fold for ring order, the tree fold), forced at small sizes by
+    ar_comm_set_streaming; bit for bit against the oracle."""
+    count = n * (4096 + 8) + 5
+    with ar.Comm(n, 0) as comm:
+        ar.ar_comm_set_streaming(comm, True)
+        for dtype in ("f32", "f16", "bf16"):
+            for k, op in enumerate(("sum", "avg", "max", "min", "prod")):
+                xs = special_inputs(n, count, dtype, seed=3000 + 10 * n + k, frac=0.1)
+                hosts = [gu.host(x) for x in xs]
+                for mode in ("fused", "tree"):
+                    exp = (oracle.tree_all_reduce(hosts, dtype, op) if mode == "tree"
+                           else oracle.fold_all_reduce(hosts, dtype, op))
+                    outs, _, _ = gu.run_all_reduce(comm, xs, dtype, op, mode, inplace=k % 2 == 0)
+                    for r in range(n):
+                        gu.assert_same(outs[r], exp[r], dtype, f"streaming n={n} {dtype} {op} {mode} rank {r}")
+
+
+@pytest.mark.parametrize("dtype,ops", [("f16", ("sum", "max", "avg")), ("bf16", ("prod", "min"))])
+def test_special_values_tiled_ring_steps(dtype, ops):
+    """Special values through the tiled 16-bit ring steps (half vectors per
+    lane, fp32 partials in the workspace): 8 ranks x 16,777,003 elements in
+    place (a footprint just under the last-level cache: cached steps) and out
+    of place (streaming steps), then the stepwise reduce-scatter at 8 x
+    2,100,008 out (streaming)."""
+    from test_gpu_parity import _reduce_scatter
+    n, count = 8, 16_777_003
+    with ar.Comm(n, 0) as comm:
+        ws = gu.attach_workspace(comm, ar.AR_COLL_ALL_REDUCE, n, count, dtype, "stepwise")
+        for k, op in enumerate(ops):
+            xs = special_inputs(n, count, dtype, seed=4000 + k, frac=0.05)
+            exp = oracle.fold_all_reduce([gu.host(x) for x in xs], dtype, op)
+            for inplace in (True, False):
+                outs, send, recv = gu.run_all_reduce(comm, xs, dtype, op, "stepwise", inplace=inplace)
+                del send, recv
+                for r in range(n):
+                    gu.assert_same(outs[r], exp[r], dtype, f"tiled steps {dtype} {op} inplace={inplace} rank {r}")
+            del xs, exp, outs
+        ar.ar_comm_set_workspace(comm, None)
+        del ws
+        rc = 2_100_008
+        xs = special_inputs(n, n * rc, dtype, seed=4100, frac=0.05)
+        exp = oracle.reduce_scatter([gu.host(x) for x in xs], dtype, ops[0])
+        got = _reduce_scatter(comm, xs, dtype, ops[0], "stepwise", False)
+        for r in range(n):
+            gu.assert_same(got[r], exp[r], dtype, f"tiled RS steps {dtype} {ops[0]} rank {r}")
+    del xs, exp, got
+    torch.cuda.empty_cache()
