@@ -55,11 +55,13 @@ def test_special_values(n, dtype, mode):
                     gu.assert_same(outs[r], exp[r], dtype, f"n={n} {dtype} {op} {mode} frac={frac} rank {r}")
 
 
+@pytest.mark.parametrize("streaming", (False, True))
 @pytest.mark.parametrize("dtype", ("f32", "f16", "bf16"))
-def test_special_values_multi_and_scatter(dtype):
+def test_special_values_multi_and_scatter(dtype, streaming):
     n = 8
     count = n * (4096 + 8)
     with ar.Comm(n, 0) as comm:
+        ar.ar_comm_set_streaming(comm, streaming)
         for k, op in enumerate(("sum", "max", "min", "prod")):
             xs = special_inputs(n, count, dtype, seed=77 + k, frac=0.3)
             hosts = [gu.host(x) for x in xs]
@@ -75,7 +77,7 @@ def test_special_values_multi_and_scatter(dtype):
             torch.cuda.synchronize()
             for r in range(n):
                 got = np.concatenate([gu.host(bufs[t][r].view) for t in range(len(sizes))])
-                gu.assert_same(got, exp[r], dtype, f"multi {dtype} {op} rank {r}")
+                gu.assert_same(got, exp[r], dtype, f"multi {dtype} {op} streaming={streaming} rank {r}")
             # reduce-scatter: rank r gets chunk r of the all-reduce
             q = count // n
             rs_exp = oracle.reduce_scatter(hosts, dtype, op)
@@ -83,7 +85,7 @@ def test_special_values_multi_and_scatter(dtype):
             ar.ar_reduce_scatter(comm, [x.data_ptr() for x in xs], [b.ptr() for b in recv], q, dtype, op, "fused")
             torch.cuda.synchronize()
             for r in range(n):
-                gu.assert_same(gu.host(recv[r].view), rs_exp[r], dtype, f"rs {dtype} {op} rank {r}")
+                gu.assert_same(gu.host(recv[r].view), rs_exp[r], dtype, f"rs {dtype} {op} streaming={streaming} rank {r}")
                 gu.assert_same(gu.host(recv[r].view), exp[r][r * q:(r + 1) * q], dtype, f"rs vs ar rank {r}")
 
 
